@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise low-bit codec on one MI355X.
+
+Workload: one 64 Mi-element binary32 gradient bucket (Student-t with 3
+degrees of freedom, times 1e-3, seed 1), block 256, stochastic rounding keyed
+by seed 42, bitwidths 1, 2, 4 and 8.  One step is one pass of the whole hot
+path over that bucket, as the single-GPU share of a low-bit data-parallel
+exchange:
+
+  for b in (1, 2, 4, 8):
+      compress the bucket                      (quantize + pack, SR)
+      local reduce of this GPU's 8 Mi share:   8 peer chunks (the 8 slices of
+                                               the packed bucket) decoded,
+                                               summed in peer order, recompressed
+      decompress the bucket                    (unpack + dequantize)
+  error-feedback compress of the bucket        (b = 4, residual carried over steps)
+  weight-difference compress + apply           (64 Mi bfloat16 shard, b = 4, B = 64)
+
+`value` counts full-precision (binary32-equivalent) bytes through the step's
+15 stage passes -- each stage touches the 64 Mi elements once -- divided by
+the step time.  Inputs are resident in HBM before the timed region.
+
+The `roofline` object covers the kernel with the largest share of the step,
+timed with HIP events on the stream the kernels run on; `traffic` comes from
+the committed rocprofv3 counter summary when it was taken on the current
+kernel sources.  `cpu_baseline` times the CPU oracle on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BITS = (1, 2, 4, 8)
+BLOCK = 256
+SEED = 42
+PEERS = 8
+W_BITS, W_BLOCK = 4, 64
+EF_BITS = 4
+METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HBM peak"
+
+# demangled kernel names as rocprofv3 reports them
+def kname_quant(bits, log2b, sr, dt, mode):
+    return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}>" \
+           f"(lowbit::QuantArgs)"
+
+
+def kname_reduce(bits, log2b, sr):
+    return f"void lowbit::reduce_kernel<{bits}, {log2b}, {str(sr).lower()}>(lowbit::ReduceArgs)"
+
+
+def kname_dequant(bits, apply, dt):
+    return f"void lowbit::dequant_kernel<{bits}, {apply}, {dt}>(lowbit::DequantArgs)"
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "weight_communication_compression_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "lowbit.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none for the current sources."""
+    digest = source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic:"):
+                continue
+            f = dict(kv.split("=", 1) for kv in line[len("traffic:"):].strip().split(" | ")[1:])
+            name = line[len("traffic:"):].strip().split(" | ")[0]
+            if name == kernel and f.get("source") == digest:
+                return float(f["bytes_per_launch"])
+    return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample", type=int, default=32 << 20,
+                    help="elements of the bucket the CPU oracle processes (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the codec shards by block-aligned ranges; collectives are not built)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from weight_communication_compression_amd import lowbit as L
+    from weight_communication_compression_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = L.lib()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    # ------------------------------------------------------------ inputs --
+    N = synth.BUCKET_N
+    share = N // PEERS
+    x_host = synth.bucket_input(N)
+    w_prev_h, w_new_h = synth.weight_pair(N)
+    x = torch.from_numpy(x_host).to(dev)
+    w_prev = torch.from_numpy(w_prev_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    w_new = torch.from_numpy(w_new_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    resid = torch.zeros(N, dtype=torch.float32, device=dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    w_out = torch.empty_like(w_prev)
+
+    def qp(bits, block, sr=False, seed=0, off=0):
+        return L.QParams(bits, block, int(sr), 0, seed, off)
+
+    P = ctypes.c_void_p
+    stages = []      # (name, kernel name, algorithmic bytes, callable)
+    keep = []        # keep ctypes objects alive
+
+    for b in BITS:
+        nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
+        codes = torch.empty(nw, dtype=torch.int32, device=dev)
+        scales = torch.empty(nb, dtype=torch.float16, device=dev)
+        q = qp(b, BLOCK, True, SEED, 0)
+        keep += [codes, scales, q]
+        a = (P(x.data_ptr()), L.F32, N, ctypes.byref(q), P(codes.data_ptr()),
+             P(scales.data_ptr()), sh)
+        stages.append((f"quantize_pack b{b}", kname_quant(b, 8, b > 1, 0, 0),
+                       N * 4 + nw * 4 + nb * 2, (lib.lowbit_quantize_pack, a)))
+
+        snw, snb = L.num_words(share, b), L.num_blocks(share, BLOCK)
+        cp = (P * PEERS)(*[codes.data_ptr() + p * snw * 4 for p in range(PEERS)])
+        spp = (P * PEERS)(*[scales.data_ptr() + p * snb * 2 for p in range(PEERS)])
+        rc = torch.empty(snw, dtype=torch.int32, device=dev)
+        rs = torch.empty(snb, dtype=torch.float16, device=dev)
+        qi, qo = qp(b, BLOCK), qp(b, BLOCK)
+        keep += [cp, spp, rc, rs, qi, qo]
+        a = (ctypes.cast(cp, P), ctypes.cast(spp, P), PEERS, share, ctypes.byref(qi),
+             ctypes.byref(qo), P(rc.data_ptr()), P(rs.data_ptr()), None, sh)
+        stages.append((f"reduce_requant b{b}", kname_reduce(b, 8, False),
+                       (PEERS + 1) * (snw * 4 + snb * 2), (lib.lowbit_reduce_requant, a)))
+
+        qd = qp(b, BLOCK)
+        keep.append(qd)
+        a = (P(codes.data_ptr()), P(scales.data_ptr()), N, ctypes.byref(qd), P(y.data_ptr()), sh)
+        stages.append((f"unpack_dequant b{b}", kname_dequant(b, 0, 0),
+                       nw * 4 + nb * 2 + N * 4, (lib.lowbit_unpack_dequant, a)))
+
+    nw, nb = L.num_words(N, EF_BITS), L.num_blocks(N, BLOCK)
+    ec = torch.empty(nw, dtype=torch.int32, device=dev)
+    es = torch.empty(nb, dtype=torch.float16, device=dev)
+    qe = qp(EF_BITS, BLOCK, True, SEED, 0)
+    keep += [ec, es, qe]
+    a = (P(x.data_ptr()), L.F32, P(resid.data_ptr()), N, ctypes.byref(qe), P(ec.data_ptr()),
+         P(es.data_ptr()), sh)
+    stages.append((f"ef_compress b{EF_BITS}", kname_quant(EF_BITS, 8, True, 0, 1),
+                   3 * N * 4 + nw * 4 + nb * 2, (lib.lowbit_ef_compress, a)))
+
+    nw, nb = L.num_words(N, W_BITS), L.num_blocks(N, W_BLOCK)
+    wc = torch.empty(nw, dtype=torch.int32, device=dev)
+    ws = torch.empty(nb, dtype=torch.float16, device=dev)
+    qw = qp(W_BITS, W_BLOCK)
+    keep += [wc, ws, qw]
+    a = (P(w_new.data_ptr()), P(w_prev.data_ptr()), L.BF16, N, ctypes.byref(qw), P(wc.data_ptr()),
+         P(ws.data_ptr()), sh)
+    stages.append((f"wdiff_compress b{W_BITS}", kname_quant(W_BITS, 6, False, 1, 2),
+                   2 * N * 2 + nw * 4 + nb * 2, (lib.lowbit_wdiff_compress, a)))
+    a = (P(w_prev.data_ptr()), P(wc.data_ptr()), P(ws.data_ptr()), N, ctypes.byref(qw),
+         P(w_out.data_ptr()), L.BF16, sh)
+    stages.append((f"wdiff_apply b{W_BITS}", kname_dequant(W_BITS, 1, 1),
+                   2 * N * 2 + nw * 4 + nb * 2, (lib.lowbit_wdiff_apply, a)))
+
+    full_precision_bytes = len(stages) * N * 4
+
+    def run(fn_args):
+        fn, a = fn_args
+        st = fn(*a)
+        if st != 0:
+            raise L.LowbitError(st, fn.__name__)
+
+    def step(timed_index=None, ev=None):
+        for i, (_, _, _, fa) in enumerate(stages):
+            if i == timed_index:
+                ev[0].record(stream)
+                run(fa)
+                ev[1].record(stream)
+            else:
+                run(fa)
+
+    # ------------------------------------------------------------ warmup --
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    # per-stage durations (untimed pass) to find the dominant kernel
+    per_stage = []
+    for i in range(len(stages)):
+        evs = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            step(i, (e0, e1))
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        per_stage.append(sorted(e0.elapsed_time(e1) for e0, e1 in evs)[2])
+    dom = max(range(len(stages)), key=lambda i: per_stage[i])
+
+    # ------------------------------------------------------------- timed --
+    resid.zero_()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(dom, evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    value = full_precision_bytes / (ms_per_step * 1e-3) / 1e9
+
+    name, kname, alg_bytes, _ = stages[dom]
+    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(kname)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": kname, "stage": name,
+                "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes}
+    kernels = {s[0]: {"us": round(per_stage[i] * 1e3, 2),
+                      "alg_GBps": round(s[2] / (per_stage[i] * 1e-3) / 1e9, 1),
+                      "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+               for i, s in enumerate(stages)}
+
+    # ------------------------------------------------------- CPU oracle --
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(x_host, w_prev_h, w_new_h, min(args.cpu_sample, N), len(stages))
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "gradient bucket: 64Mi fp32 Student-t(3) x 1e-3 (seed 1), block 256, "
+                        "SR seed 42, bits 1/2/4/8; step = compress + 8-peer local reduce of "
+                        "the 8Mi share + decompress per bitwidth, EF compress (b4), weight-diff "
+                        "compress+apply (64Mi bf16, b4 B64)",
+            "elements": N, "block_size": BLOCK, "bitwidths": list(BITS), "peers": PEERS,
+            "value_counts": "binary32-equivalent bytes of the 15 stage passes / step time",
+            "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(x, w_prev, w_new, n, nstages):
+    """Time the CPU oracle over the first n elements of the same workload
+    (all 15 stage passes), single-threaded; report in the same unit."""
+    import numpy as np
+    import oracle as O
+
+    xs = np.ascontiguousarray(x[:n])
+    wp, wn = np.ascontiguousarray(w_prev[:n]), np.ascontiguousarray(w_new[:n])
+    share = n // PEERS
+    t0 = time.perf_counter()
+    for b in BITS:
+        c, s = O.quantize_pack(xs, b, BLOCK, True, SEED, 0)
+        snw, snb = O.num_words(share, b), O.num_blocks(share, BLOCK)
+        O.reduce_requant([c[p * snw:(p + 1) * snw] for p in range(PEERS)],
+                         [s[p * snb:(p + 1) * snb] for p in range(PEERS)], share, b, BLOCK, b)
+        O.unpack_dequant(c, s, n, b, BLOCK)
+    O.ef_compress(xs, np.zeros(n, np.float32), EF_BITS, BLOCK, True, SEED, 0)
+    c, s = O.wdiff_compress(wn, wp, W_BITS, W_BLOCK)
+    O.wdiff_apply(wp, c, s, W_BITS, W_BLOCK)
+    dt = time.perf_counter() - t0
+    return {"value": round(nstages * n * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n} elements of the bucket (and of the weight shard), all "
+                      f"{nstages} stage passes, scalar C oracle, one thread"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,192 @@
+/*
+ * lowbit.h -- C ABI of liblowbit: blockwise low-bit compression of training
+ * communication buffers on AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the codec stages of a low-bit data-parallel exchange:
+ *
+ *   compress   : buffer -> one binary16 scale per block + b-bit codes packed
+ *                LSB-first into 32-bit words          (bitscom README,
+ *                "Implemented Features": blockwise quantization with per-block
+ *                FP16 scales; 1/2/4/8-bit codes; bit-packing; stochastic
+ *                rounding; compress/decompress helpers)
+ *   decompress : codes + scales -> binary32            (same section)
+ *   error-feedback compress: compress (g + e), keep e <- (g + e) - deq(...)
+ *                (bitscom README, "Implemented Features" and "Backend
+ *                Registration Options": the legacy mode on the first-stage
+ *                quantization)
+ *   local reduce + requantize: the middle stage of a low-bit all-reduce
+ *                (all-to-all -> local reduce -> all-gather; bitscom README,
+ *                "Implemented Features")
+ *   weight-difference compress / apply (SDP4Bit README, "Overview" and
+ *                "Weight Quantization Arguments")
+ *
+ * Wire format (shared by every entry point):
+ *   codes  : uint32_t[lowbit_num_words(n, b)], little-endian words; element i
+ *            occupies bits [(i mod 32/b) * b, +b) of word i / (32/b); bits of
+ *            the last word past element n-1 are 0.  For b >= 2 the stored code
+ *            is u = q + 2^(b-1) with q in [-(2^(b-1)-1), 2^(b-1)-1]; for b = 1
+ *            it is u = 1 for x >= 0 (including -0.0) and 0 otherwise.
+ *   scales : uint16_t[lowbit_num_blocks(n, B)], binary16 bit patterns, one per
+ *            block of B consecutive elements (the last block may be shorter).
+ *            b >= 2: s = smallest binary16 >= fl(max|x| / (2^(b-1)-1));
+ *            b = 1 : s = smallest binary16 >= fl(sum|x| / n_valid), the sum
+ *            taken over the block by an adjacent-pairs tree; both saturate at
+ *            65504.  Dequantized value: q * s (b >= 2), u ? s : -s (b = 1).
+ *   rounding: v = fl(x * fl(1/s)); round to nearest (ties to even) or
+ *            stochastic q = floor(fl(v + r)), r = (h >> 8) * 2^-24 with
+ *            h = fmix32(lo32(i) ^ fmix32(hi32(i) ^ K(seed))), i the global
+ *            element index (index_offset + position), fmix32 the MurmurHash3
+ *            finaliser and K(seed) = fmix32(lo32(seed) ^ fmix32(hi32(seed) ^
+ *            0x9E3779B9)); then q is clamped to the grid.
+ *
+ * Conventions:
+ *   - Pointers named as device pointers must be device memory (HBM) visible to
+ *     the current HIP device; `peer_codes` / `peer_scales` themselves are host
+ *     arrays holding device pointers.  The caller allocates and owns every
+ *     buffer, including the error-feedback residual; the library allocates
+ *     nothing and keeps no state between calls.
+ *   - Alignment: element buffers (x, g, residual, w_*, y) 16 bytes, codes
+ *     4 bytes, scales 2 bytes.
+ *   - Launches are asynchronous on `stream` (0 = the null stream).  Argument
+ *     errors are reported synchronously and nothing is launched.  A launch
+ *     failure returns LOWBIT_EDEVICE.  No call aborts or throws.
+ *   - n == 0 is a no-op returning LOWBIT_OK.
+ *   - Outputs must not alias inputs, except `residual` (in/out by design) and
+ *     w_out == w_old in lowbit_wdiff_apply.
+ *   - Non-finite inputs give unspecified (but in-range) codes; calls still
+ *     terminate normally.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LOWBIT_OK = 0,
+    LOWBIT_EINVAL = 1,        /* invalid argument; nothing launched            */
+    LOWBIT_EUNSUPPORTED = 2,  /* valid but not built into this library         */
+    LOWBIT_EDEVICE = 3        /* the HIP runtime reported a launch error       */
+} lowbit_status;
+
+typedef enum {
+    LOWBIT_F32 = 0,           /* IEEE binary32                                 */
+    LOWBIT_BF16 = 1           /* bfloat16, widened exactly to binary32         */
+} lowbit_dtype;
+
+/* Quantizer options (bitscom README, "Backend Registration Options": bitwidth
+ * and block size; "Implemented Features": stochastic rounding). */
+typedef struct {
+    int32_t  bitwidth;        /* b: 1, 2, 4 or 8                                */
+    int32_t  block_size;      /* B: power of two in [32, 4096]                  */
+    int32_t  stochastic;      /* 0: nearest, ties to even; 1: stochastic
+                                 rounding (ignored when b == 1)                 */
+    int32_t  reserved;        /* must be 0                                      */
+    uint64_t seed;            /* stochastic-rounding key                        */
+    uint64_t index_offset;    /* global index of element 0; a multiple of B.
+                                 Only the random numbers depend on it, so a
+                                 buffer split at block boundaries and
+                                 compressed in pieces gives the same bytes.    */
+} lowbit_qparams;
+
+/* ceil(n * b / 32), or -1 for invalid arguments. */
+int64_t lowbit_num_words(int64_t n, int32_t bitwidth);
+/* ceil(n / B), or -1 for invalid arguments. */
+int64_t lowbit_num_blocks(int64_t n, int32_t block_size);
+/* static, human-readable name of a status code */
+const char* lowbit_status_string(lowbit_status status);
+/* library version string, e.g. "lowbit 0.1.0 gfx950" */
+const char* lowbit_version(void);
+
+/*
+ * Compress (bitscom README, "Implemented Features": blockwise FP16-scaled
+ * quantization to 1/2/4/8 bits with bit-packing, optional stochastic
+ * rounding).
+ *   x      : device, n elements of type xt
+ *   codes  : device, lowbit_num_words(n, p->bitwidth) words (written)
+ *   scales : device, lowbit_num_blocks(n, p->block_size) binary16 (written)
+ * EINVAL: p == NULL, bad bitwidth/block_size/reserved, index_offset not a
+ * multiple of block_size, n < 0, NULL or misaligned pointer with n > 0,
+ * unknown dtype.
+ */
+lowbit_status lowbit_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
+                                   const lowbit_qparams* p, uint32_t* codes, uint16_t* scales,
+                                   hipStream_t stream);
+
+/*
+ * Decompress (bitscom README, "Implemented Features": unpacking and
+ * dequantization, the decompress helper).
+ *   codes, scales : device, as written by a compress call with the same
+ *                   bitwidth and block_size (seed/index_offset/stochastic are
+ *                   not used)
+ *   y             : device, n binary32 values (written); y_i = q_i * s, exact.
+ */
+lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t n,
+                                    const lowbit_qparams* p, float* y, hipStream_t stream);
+
+/*
+ * Error-feedback compress, legacy mode (bitscom README, "Implemented
+ * Features": error feedback in first-stage quantization; "Backend
+ * Registration Options": legacy mode).  For every element
+ *     a = fl(g + e);  (codes, scales) = compress(a);  e <- fl(a - deq)
+ *   g        : device, n elements of type gt (read)
+ *   residual : device, n binary32 (read and overwritten); zero it before the
+ *              first step.
+ */
+lowbit_status lowbit_ef_compress(const void* g, lowbit_dtype gt, float* residual, int64_t n,
+                                 const lowbit_qparams* p, uint32_t* codes, uint16_t* scales,
+                                 hipStream_t stream);
+
+/*
+ * Local reduce + requantize of a low-bit all-reduce (bitscom README,
+ * "Implemented Features": all-to-all -> local reduce -> all-gather).  The
+ * npeers chunks cover the same n elements; each is dequantized with in_p and
+ * summed in binary32 in peer order,
+ *     acc = d_0;  acc = fl(acc + d_p), p = 1 .. npeers-1,
+ * and acc is compressed with out_p.
+ *   peer_codes, peer_scales : HOST arrays of npeers DEVICE pointers
+ *   out_sum                 : device, n binary32 (written) or NULL to skip
+ * EINVAL additionally: npeers outside [1, 16], in_p->block_size !=
+ * out_p->block_size.  EUNSUPPORTED: in_p->bitwidth != out_p->bitwidth.
+ */
+lowbit_status lowbit_reduce_requant(const uint32_t* const* peer_codes,
+                                    const uint16_t* const* peer_scales, int32_t npeers, int64_t n,
+                                    const lowbit_qparams* in_p, const lowbit_qparams* out_p,
+                                    uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
+                                    hipStream_t stream);
+
+/*
+ * Weight-difference compress (SDP4Bit README, "Overview": weights are sent
+ * as quantized differences; "Weight Quantization Arguments": bit count and
+ * group size).  d = fl(w_new - w_old) is compressed with p.
+ *   w_new, w_old : device, n elements of type wt
+ */
+lowbit_status lowbit_wdiff_compress(const void* w_new, const void* w_old, lowbit_dtype wt,
+                                    int64_t n, const lowbit_qparams* p, uint32_t* codes,
+                                    uint16_t* scales, hipStream_t stream);
+
+/*
+ * Weight-difference apply, the receiving side of the same scheme:
+ *     w_out = to_wt(fl(w_old + deq)),  to_wt = identity (F32) or RNE (BF16).
+ *   w_old, w_out : device, n elements of type wt; w_out may equal w_old.
+ */
+lowbit_status lowbit_wdiff_apply(const void* w_old, const uint32_t* codes, const uint16_t* scales,
+                                 int64_t n, const lowbit_qparams* p, void* w_out, lowbit_dtype wt,
+                                 hipStream_t stream);
+
+/*
+ * Measurement aid, not a step of the method: y[i] = x[i] for n binary32
+ * values, with the same launch shape as the codec kernels.  Used to measure
+ * the achievable HBM copy bandwidth and to scale hardware byte counters.
+ */
+lowbit_status lowbit_copy_f32(const float* x, float* y, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

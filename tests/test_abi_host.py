@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every entry point ``include/lowbit.h`` declares,
+computes sizes, and rejects invalid arguments before making any HIP call.
+No test here launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_communication_compression_amd import lowbit as lb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowbit.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lowbit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "lowbit_quantize_pack" in names and len(names) >= 11
+    L = ctypes.CDLL(lb.library_path)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert lb.lib().lowbit_version().startswith(b"lowbit ")
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported combination"),
+                       (3, b"device launch error"), (99, b"unknown status")]:
+        assert lb.lib().lowbit_status_string(code) == text
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 31, 32, 33, 1 << 20, (1 << 40) + 3])
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_num_words(n, bits):
+    assert lb.num_words(n, bits) == (n * bits + 31) // 32
+
+
+@pytest.mark.parametrize("B", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+def test_num_blocks(B):
+    for n in [0, 1, B - 1, B, B + 1, 1000 * B + 17]:
+        assert lb.num_blocks(n, B) == -(-n // B)
+
+
+def test_size_helpers_reject():
+    L = lb.lib()
+    for bits in [0, 3, 5, 16, -1]:
+        assert L.lowbit_num_words(10, bits) == -1
+    for B in [0, 16, 48, 8192, 100]:
+        assert L.lowbit_num_blocks(10, B) == -1
+    assert L.lowbit_num_words(-1, 4) == -1
+
+
+def _qp(**kw):
+    d = dict(bitwidth=4, block_size=128, stochastic=0, reserved=0, seed=0, index_offset=0)
+    d.update(kw)
+    return lb.QParams(**d)
+
+
+BAD_PARAMS = [dict(bitwidth=3), dict(bitwidth=16), dict(block_size=16), dict(block_size=96),
+              dict(block_size=8192), dict(index_offset=64), dict(reserved=1)]
+
+
+@pytest.mark.parametrize("bad", BAD_PARAMS)
+def test_entry_points_reject_bad_params(bad):
+    """Every entry point returns EINVAL for invalid options, before any HIP call
+    (the pointers passed are NULL, so nothing could be launched anyway)."""
+    L = lb.lib()
+    qp = _qp(**bad)
+    r = ctypes.byref(qp)
+    assert L.lowbit_quantize_pack(None, 0, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_unpack_dequant(None, None, 100, r, None, None) == lb.EINVAL
+    assert L.lowbit_ef_compress(None, 0, None, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_wdiff_compress(None, None, 0, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_wdiff_apply(None, None, None, 100, r, None, 0, None) == lb.EINVAL
+    good = _qp()
+    assert L.lowbit_reduce_requant(None, None, 2, 100, r, ctypes.byref(good), None, None, None,
+                                   None) == lb.EINVAL
+    assert L.lowbit_reduce_requant(None, None, 2, 100, ctypes.byref(good), r, None, None, None,
+                                   None) == lb.EINVAL
+
+
+def test_entry_points_reject_null_params_struct():
+    L = lb.lib()
+    assert L.lowbit_quantize_pack(None, 0, 100, None, None, None, None) == lb.EINVAL
+    assert L.lowbit_unpack_dequant(None, None, 100, None, None, None) == lb.EINVAL
+
+
+def test_null_pointers_and_negative_sizes():
+    L = lb.lib()
+    r = ctypes.byref(_qp())
+    assert L.lowbit_quantize_pack(None, 0, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_quantize_pack(None, 0, -1, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_quantize_pack(None, 7, 100, r, None, None, None) == lb.EINVAL   # dtype
+    assert L.lowbit_ef_compress(None, 1, None, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_copy_f32(None, None, 10, None) == lb.EINVAL
+    assert L.lowbit_copy_f32(None, None, -10, None) == lb.EINVAL
+
+
+def test_misaligned_pointers_rejected():
+    """Misaligned (never dereferenced) addresses are rejected on the host."""
+    L = lb.lib()
+    r = ctypes.byref(_qp())
+    odd = ctypes.c_void_p(0x1008)        # 8-aligned, not 16-aligned
+    ok4 = ctypes.c_void_p(0x2000)
+    ok2 = ctypes.c_void_p(0x3000)
+    assert L.lowbit_quantize_pack(odd, 0, 100, r, ok4, ok2, None) == lb.EINVAL
+    assert L.lowbit_quantize_pack(ok4, 0, 100, r, ctypes.c_void_p(0x2002), ok2, None) == lb.EINVAL
+    assert L.lowbit_quantize_pack(ok4, 0, 100, r, ok4, ctypes.c_void_p(0x3001), None) == lb.EINVAL
+    assert L.lowbit_unpack_dequant(ok4, ok2, 100, r, odd, None) == lb.EINVAL
+
+
+def test_zero_length_is_a_noop():
+    L = lb.lib()
+    r = ctypes.byref(_qp())
+    assert L.lowbit_quantize_pack(None, 0, 0, r, None, None, None) == lb.OK
+    assert L.lowbit_unpack_dequant(None, None, 0, r, None, None) == lb.OK
+    assert L.lowbit_ef_compress(None, 0, None, 0, r, None, None, None) == lb.OK
+    assert L.lowbit_wdiff_compress(None, None, 1, 0, r, None, None, None) == lb.OK
+    assert L.lowbit_wdiff_apply(None, None, None, 0, r, None, 1, None) == lb.OK
+    assert L.lowbit_reduce_requant(None, None, 1, 0, r, r, None, None, None, None) == lb.OK
+    assert L.lowbit_copy_f32(None, None, 0, None) == lb.OK
+
+
+def test_reduce_argument_rules():
+    L = lb.lib()
+    r = ctypes.byref(_qp())
+    for npeers in [0, -1, 17, 100]:
+        assert L.lowbit_reduce_requant(None, None, npeers, 10, r, r, None, None, None,
+                                       None) == lb.EINVAL
+    other_block = ctypes.byref(_qp(block_size=256))
+    assert L.lowbit_reduce_requant(None, None, 2, 10, r, other_block, None, None, None,
+                                   None) == lb.EINVAL
+    other_bits = ctypes.byref(_qp(bitwidth=8))
+    assert L.lowbit_reduce_requant(None, None, 2, 10, r, other_bits, None, None, None,
+                                   None) == lb.EUNSUPPORTED
+    # a NULL entry in the peer pointer arrays is rejected before launch
+    ok = ctypes.c_void_p(0x4000)
+    cp = (ctypes.c_void_p * 2)(ok, None)
+    sp = (ctypes.c_void_p * 2)(ok, ok)
+    assert L.lowbit_reduce_requant(ctypes.cast(cp, ctypes.c_void_p),
+                                   ctypes.cast(sp, ctypes.c_void_p), 2, 10, r, r, ok, ok, None,
+                                   None) == lb.EINVAL
+
+
+def test_binding_rejects_host_tensors_and_bad_outputs():
+    import torch
+    x = torch.zeros(256)
+    with pytest.raises(lb.LowbitError):
+        lb.quantize_pack(x, 4, 128)
+    with pytest.raises(lb.LowbitError):
+        lb.quantize_pack(x, 3, 128)
+    with pytest.raises(lb.LowbitError):      # undersized codes buffer
+        lb.quantize_pack(x, 4, 128, codes=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(lb.LowbitError):      # wrong scales dtype
+        lb.quantize_pack(x, 4, 128, codes=torch.zeros(32, dtype=torch.int32),
+                         scales=torch.zeros(2, dtype=torch.float32))
+    with pytest.raises(lb.LowbitError):
+        lb.unpack_dequant(torch.zeros(3, dtype=torch.int32), torch.zeros(2, dtype=torch.float16),
+                          256, 4, 128)

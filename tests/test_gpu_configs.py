@@ -1,0 +1,163 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle checks whole buffers where it finishes in
+seconds (2^20 roundtrip, the 64 Mi gradient bucket at four bitwidths, the
+8 x 32 Mi local reduce) and sampled blocks elsewhere (5-step error feedback on
+128 Mi bfloat16 gradients, the 840 Mi bfloat16 weight shard).  Sampled blocks
+are recomputed by the oracle from the same host inputs with the block's global
+index offset, so the stochastic rounding sees the same counters.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import (assert_close_scaled, assert_same, bf16_np, codes_np, f32_np, say,
+                      sample_blocks, scale_per_element, scales_np, to_gpu, word_range)
+from weight_communication_compression_amd import lowbit as L
+from weight_communication_compression_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    L.lib()
+    O.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_roundtrip_2p20_b4_B128():
+    x = synth.roundtrip_input()
+    say("roundtrip 2^20 fp32 b4 B128 RTN")
+    c, s = L.quantize_pack(to_gpu(x), 4, 128)
+    y = L.unpack_dequant(c, s, x.size, 4, 128)
+    torch.cuda.synchronize()
+    wc, ws = O.quantize_pack(x, 4, 128)
+    assert_same(scales_np(s), ws, "scales")
+    assert_same(codes_np(c), wc, "codes")
+    wy = O.unpack_dequant(wc, ws, x.size, 4, 128)
+    assert_close_scaled(f32_np(y), wy, scale_per_element(ws, x.size, 128), "deq")
+    assert_same(f32_np(y), wy, "deq")
+
+
+@pytest.fixture(scope="module")
+def bucket():
+    say("generating the 64 Mi Student-t gradient bucket")
+    x = synth.bucket_input()
+    return x, to_gpu(x)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_bucket_64mi_sr_seed42_B256(bucket, bits):
+    x, gx = bucket
+    say(f"bucket 64Mi bits={bits} B256 SR seed 42")
+    c, s = L.quantize_pack(gx, bits, 256, True, 42, 0)
+    y = L.unpack_dequant(c, s, x.size, bits, 256)
+    torch.cuda.synchronize()
+    wc, ws = O.quantize_pack(x, bits, 256, True, 42, 0)
+    assert_same(scales_np(s), ws, "scales")
+    assert_same(codes_np(c), wc, "codes")
+    # decompress checked on sampled blocks (the oracle's decompress of the
+    # whole bucket is slow and adds nothing the small tests do not cover)
+    yn = f32_np(y)
+    for k in sample_blocks(ws.size, 2000, bits):
+        lo, hi = k * 256, min(x.size, (k + 1) * 256)
+        a, b = word_range(k, 256, bits, x.size)
+        want = O.unpack_dequant(wc[a:b], ws[k:k + 1], hi - lo, bits, 256)
+        assert_same(yn[lo:hi], want, f"deq block {k}")
+
+
+def test_error_feedback_5_steps_128mi_bf16():
+    n, B, bits = synth.EF_N, 128, 4
+    blocks = sample_blocks(n // B, 3000, 7)
+    e_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    e_ref = {int(k): np.zeros(B, np.float32) for k in blocks}
+    for step in range(synth.EF_STEPS):
+        g = synth.ef_gradient(step)
+        say(f"ef step {step}: 128Mi bf16 b4 B128 SR seed {2 + step}")
+        c, s = L.ef_compress(to_gpu(g), e_gpu, bits, B, True, 2 + step, 0)
+        torch.cuda.synchronize()
+        cn, sn = codes_np(c), scales_np(s)
+        en = e_gpu[:].cpu().numpy()
+        for k in blocks:
+            k = int(k)
+            lo = k * B
+            wc, ws, e_ref[k] = O.ef_compress(g[lo:lo + B], e_ref[k], bits, B, True, 2 + step, lo)
+            a, b = word_range(k, B, bits, n)
+            assert_same(cn[a:b], wc, f"codes step {step} block {k}")
+            assert sn[k] == ws[0], f"scale step {step} block {k}"
+            assert_same(en[lo:lo + B], e_ref[k], f"residual step {step} block {k}")
+        del c, s
+
+
+@pytest.fixture(scope="module")
+def peers():
+    n, B = synth.PEER_N, 128
+    pcs, pss = [], []
+    for p in range(synth.PEERS):
+        say(f"oracle quantizes peer {p} (32Mi fp32 b4 B128)")
+        c, s = O.quantize_pack(synth.peer_input(p), 4, B)
+        pcs.append(c)
+        pss.append(s)
+    return pcs, pss
+
+
+def test_peer_chunks_quantize_sampled(peers):
+    """The setup step (each peer's compress) on the GPU, sampled blocks."""
+    pcs, pss = peers
+    for p in (0, 7):
+        x = synth.peer_input(p)
+        say(f"peer {p} compress on GPU")
+        c, s = L.quantize_pack(to_gpu(x), 4, 128)
+        torch.cuda.synchronize()
+        assert_same(scales_np(s), pss[p], "scales")
+        cn = codes_np(c)
+        for k in sample_blocks(pss[p].size, 2000, p):
+            a, b = word_range(int(k), 128, 4, x.size)
+            assert_same(cn[a:b], pcs[p][a:b], f"peer {p} block {k}")
+
+
+def test_local_reduce_8x32mi_b4_B128(peers):
+    pcs, pss = peers
+    n = synth.PEER_N
+    gc = [torch.from_numpy(c.view(np.int32)).cuda() for c in pcs]
+    gs = [torch.from_numpy(s.view(np.float16)).cuda() for s in pss]
+    say("local reduce 8 x 32Mi b4 B128 RTN (+ sum)")
+    c, s, tot = L.reduce_requant(gc, gs, n, 4, 128, want_sum=True)
+    torch.cuda.synchronize()
+    say("oracle local reduce")
+    wc, ws, wt = O.reduce_requant(pcs, pss, n, 4, 128, 4, want_sum=True)
+    assert_same(scales_np(s), ws, "scales")
+    assert_same(codes_np(c), wc, "codes")
+    assert_same(f32_np(tot), wt, "sum")
+    say("local reduce without the sum output")
+    c2, s2, _ = L.reduce_requant(gc, gs, n, 4, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, c) and torch.equal(s2, s)
+
+
+def test_weight_difference_840mi_bf16_b4_B64():
+    n, B, bits = synth.WEIGHT_N, 64, 4
+    say("generating the 840Mi bf16 weight shard pair")
+    w_prev, w_new = synth.weight_pair()
+    gp, gn = to_gpu(w_prev), to_gpu(w_new)
+    say("wdiff compress 840Mi bf16 b4 B64")
+    c, s = L.wdiff_compress(gn, gp, bits, B)
+    torch.cuda.synchronize()
+    say("wdiff apply 840Mi bf16 b4 B64")
+    out = L.wdiff_apply(gp, c, s, bits, B)
+    torch.cuda.synchronize()
+    cn, sn = codes_np(c), scales_np(s)
+    on = bf16_np(out)
+    del out, c, s
+    for k in sample_blocks(n // B, 4000, 3):
+        k = int(k)
+        lo = k * B
+        wc, ws = O.wdiff_compress(w_new[lo:lo + B], w_prev[lo:lo + B], bits, B)
+        a, b = word_range(k, B, bits, n)
+        assert_same(cn[a:b], wc, f"codes block {k}")
+        assert sn[k] == ws[0], f"scale block {k}"
+        assert_same(on[lo:lo + B], O.wdiff_apply(w_prev[lo:lo + B], wc, ws, bits, B),
+                    f"apply block {k}")

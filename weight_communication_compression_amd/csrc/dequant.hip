@@ -1,0 +1,43 @@
+// decompress, weight-difference apply and the measurement copy kernel
+#include "launch.hpp"
+#include "dequant.hpp"
+
+namespace lowbit {
+
+template <int BITS, int APPLY, int DT>
+static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
+  constexpr int E = Grid<BITS>::E;
+  const int64_t nwords = (a.n + E - 1) / E;
+  const int64_t ntiles = (nwords + kWave * kDequantRows - 1) / (kWave * kDequantRows);
+  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles(ntiles)),
+                     dim3(kBlockThreads), 0, s, a);
+  return launch_status();
+}
+
+template <int BITS>
+static lowbit_status launch_d_b(bool apply, int dt, const DequantArgs& a, hipStream_t s) {
+  if (!apply) return launch_d<BITS, 0, kF32>(a, s);
+  return dt == kF32 ? launch_d<BITS, 1, kF32>(a, s) : launch_d<BITS, 1, kBF16>(a, s);
+}
+
+lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_d_b<1>(apply, dt, a, s);
+    case 2: return launch_d_b<2>(apply, dt, a, s);
+    case 4: return launch_d_b<4>(apply, dt, a, s);
+    case 8: return launch_d_b<8>(apply, dt, a, s);
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t nvec = n / 4;
+  int64_t blocks = (nvec + 2 * kBlockThreads - 1) / (2 * kBlockThreads);
+  const int64_t cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, x, y, n);
+  return launch_status();
+}
+
+}  // namespace lowbit

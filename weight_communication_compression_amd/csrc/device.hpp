@@ -1,0 +1,233 @@
+// device.hpp -- gfx950 device helpers shared by the codec kernels.
+//
+// Wave64 only (CDNA4).  Cross-lane reductions use DPP row operations and
+// ds_swizzle, never LDS round trips.  Every floating-point step that decides
+// a code is a single IEEE binary32 operation: the library is compiled with
+// -ffp-contract=off, fp32 denormals preserved, and correctly rounded division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;              // 4 waves per workgroup
+constexpr float kMagic = 12582912.0f;           // 1.5 * 2^23
+constexpr uint32_t kMagicBits = 0x4B400000u;    // bit pattern of kMagic
+
+enum Mode : int { kPlain = 0, kErrorFeedback = 1, kWeightDiff = 2 };
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+template <int BITS>
+struct Grid {
+  static constexpr int E = 32 / BITS;                               // codes per word
+  static constexpr int QMAX = BITS == 1 ? 1 : (1 << (BITS - 1)) - 1;
+  static constexpr uint32_t HALF = BITS == 1 ? 0u : (1u << (BITS - 1));
+  // the offset bit of every field: xor with it turns offset codes into
+  // two's-complement fields
+  static constexpr uint32_t FLIP = [] {
+    uint32_t f = 0;
+    for (int j = 0; j < E; ++j) f |= HALF << (j * BITS);
+    return f;
+  }();
+  // packing constant: word = PACK_BIAS + sum_j bits(q_j + kMagic) << (j*BITS)
+  // equals sum_j (q_j + HALF) << (j*BITS) modulo 2^32, because
+  // bits(q + kMagic) = kMagicBits + q for |q| < 2^22.
+  static constexpr uint32_t PACK_BIAS = [] {
+    uint32_t c = 0;
+    for (int j = 0; j < E; ++j) c += (HALF - kMagicBits) << (j * BITS);
+    return c;
+  }();
+};
+
+// ---------------------------------------------------------------- lanes --
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int PATTERN>
+__device__ __forceinline__ float swizzle_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Reduce over aligned groups of L consecutive lanes (L a power of two <= 64);
+// every lane of a group ends with the group's result.  For the sum, the
+// combination order is the adjacent-pairs tree over the lanes: partners
+// 1, 2, 4, ... apart (quad_perm for 1 and 2; after those steps half_mirror
+// and row_mirror pair lanes with the neighbouring aligned group of 4 and 8;
+// swizzle xor 16; the two wave halves last).  Addition is commutative, so
+// which side of a pair a lane sees first does not change the bits.
+template <int L, bool SUM>
+__device__ __forceinline__ float group_reduce(float v) {
+  auto op = [](float a, float b) { return SUM ? a + b : fmaxf(a, b); };
+  if constexpr (L >= 2) v = op(v, dpp_f32<0xB1>(v));     // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v = op(v, dpp_f32<0x4E>(v));     // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v = op(v, dpp_f32<0x141>(v));    // row_half_mirror
+  if constexpr (L >= 16) v = op(v, dpp_f32<0x140>(v));   // row_mirror
+  if constexpr (L >= 32) v = op(v, swizzle_f32<0x401F>(v));  // lane ^ 16 within 32
+  if constexpr (L >= 64) v = op(readlane_f32(v, 0), readlane_f32(v, 32));
+  return v;
+}
+
+// Adjacent-pairs tree sum of |v[0..N)| within one lane (N a power of two).
+template <int N>
+__device__ __forceinline__ float lane_abs_tree(const float* v) {
+  float t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = fabsf(v[j]);
+#pragma unroll
+  for (int w = N; w > 1; w >>= 1) {
+#pragma unroll
+    for (int j = 0; j < w / 2; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+  }
+  return t[0];
+}
+
+// Adjacent-pairs tree over N values held in registers.
+template <int N>
+__device__ __forceinline__ float reg_tree(const float* g) {
+  float t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = g[j];
+#pragma unroll
+  for (int w = N; w > 1; w >>= 1) {
+#pragma unroll
+    for (int j = 0; j < w / 2; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+  }
+  return t[0];
+}
+
+// ---------------------------------------------------------------- scale --
+// Smallest binary16 value >= t (t >= 0), saturated to 65504 (0x7BFF); any
+// NaN or value above 65504 gives 0x7BFF.  v_cvt_f16_f32 rounds to nearest
+// even with fp16 denormals kept; stepping the pattern up by one gives the
+// next larger binary16 value.
+__device__ __forceinline__ uint32_t f16_round_up(float t) {
+  _Float16 h = (_Float16)t;
+  uint32_t hb = (uint32_t)__builtin_bit_cast(unsigned short, h);
+  hb += ((float)h < t) ? 1u : 0u;
+  return hb < 0x7BFFu ? hb : 0x7BFFu;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t hb) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)hb);
+}
+
+struct BlockScale {
+  uint32_t s16;   // binary16 pattern
+  float s;        // its value
+  float inv;      // fl(1 / s), or 0 when s == 0
+};
+
+// t = fl(stat / div); s16 = round-up binary16 of t.
+__device__ __forceinline__ BlockScale make_scale(float stat, float div) {
+  BlockScale r;
+  float t = stat / div;                       // correctly rounded division
+  r.s16 = f16_round_up(t);
+  r.s = f16_bits_to_f32(r.s16);
+  r.inv = (r.s != 0.0f) ? 1.0f / r.s : 0.0f;  // correctly rounded division
+  return r;
+}
+
+// ----------------------------------------------------------------- hash --
+// MurmurHash3 32-bit finaliser.
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// ---------------------------------------------------------------- loads --
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Load E consecutive elements starting at element i0 (16-byte aligned for
+// E >= 8 in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16).
+template <int DT, int E>
+__device__ __forceinline__ void load_vec(const void* base, int64_t i0, float* v) {
+  if constexpr (DT == kF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i0);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+      float4 t = p[k];
+      v[4 * k + 0] = t.x;
+      v[4 * k + 1] = t.y;
+      v[4 * k + 2] = t.z;
+      v[4 * k + 3] = t.w;
+    }
+  } else {
+    const uint16_t* b = static_cast<const uint16_t*>(base) + i0;
+    if constexpr (E == 4) {
+      uint2 t = *reinterpret_cast<const uint2*>(b);
+      v[0] = bf16_lo(t.x);
+      v[1] = bf16_hi(t.x);
+      v[2] = bf16_lo(t.y);
+      v[3] = bf16_hi(t.y);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(b);
+#pragma unroll
+      for (int k = 0; k < E / 8; ++k) {
+        uint4 t = p[k];
+        v[8 * k + 0] = bf16_lo(t.x);
+        v[8 * k + 1] = bf16_hi(t.x);
+        v[8 * k + 2] = bf16_lo(t.y);
+        v[8 * k + 3] = bf16_hi(t.y);
+        v[8 * k + 4] = bf16_lo(t.z);
+        v[8 * k + 5] = bf16_hi(t.z);
+        v[8 * k + 6] = bf16_lo(t.w);
+        v[8 * k + 7] = bf16_hi(t.w);
+      }
+    }
+  }
+}
+
+// Guarded element-by-element load for the ragged last tile: positions at or
+// past n read as +0.
+template <int DT, int E>
+__device__ __forceinline__ void load_tail(const void* base, int64_t i0, int64_t n, float* v) {
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    int64_t i = i0 + j;
+    float x = 0.0f;
+    if (i < n) {
+      if constexpr (DT == kF32) x = static_cast<const float*>(base)[i];
+      else x = __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+    }
+    v[j] = x;
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void store_vec_f32(float* base, int64_t i0, const float* v) {
+  float4* p = reinterpret_cast<float4*>(base + i0);
+#pragma unroll
+  for (int k = 0; k < E / 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+}
+
+template <int E>
+__device__ __forceinline__ void store_tail_f32(float* base, int64_t i0, int64_t n, const float* v) {
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (i0 + j < n) base[i0 + j] = v[j];
+}
+
+// binary32 -> bfloat16, round to nearest even, by integer arithmetic.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace lowbit

@@ -1,0 +1,50 @@
+// launch.hpp -- host-side launch helpers shared by the kernel translation
+// units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lowbit.h"
+#include "args.hpp"
+
+#ifndef LOWBIT_BLOCKS_PER_CU
+#define LOWBIT_BLOCKS_PER_CU 8     // 256-thread workgroups resident per CU at most
+#endif
+
+namespace lowbit {
+
+
+// Number of compute units of the current device (cached per device id).
+int device_cu_count();
+
+// Grid for a wave-per-tile kernel: one wave per tile, at most
+// LOWBIT_BLOCKS_PER_CU workgroups per CU; the kernels loop over the rest.
+inline int grid_for_tiles(int64_t ntiles) {
+  const int64_t waves_per_block = 256 / 64;
+  int64_t blocks = (ntiles + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+inline lowbit_status launch_status() {
+  return hipGetLastError() == hipSuccess ? LOWBIT_OK : LOWBIT_EDEVICE;
+}
+
+// mode: 0 plain, 1 error feedback, 2 weight difference
+lowbit_status launch_quantize_plain(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
+                                    hipStream_t s);
+lowbit_status launch_quantize_ef(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
+                                 hipStream_t s);
+lowbit_status launch_quantize_wdiff(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
+                                    hipStream_t s);
+lowbit_status launch_reduce(int bits, int log2b, bool sr, const ReduceArgs& a, hipStream_t s);
+lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a, hipStream_t s);
+lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
+
+}  // namespace lowbit
+
+// Expand F(LOG2B) for every supported block size 2^5 .. 2^12.
+#define LOWBIT_FOR_EACH_LOG2B(F) F(5) F(6) F(7) F(8) F(9) F(10) F(11) F(12)

@@ -1,0 +1,54 @@
+// quantize_tu.hpp -- one translation unit's worth of compress-kernel
+// instantiations for the mode LOWBIT_TU_MODE, exposed through the launcher
+// LOWBIT_TU_LAUNCHER(bits, log2b, sr, dtype, args, stream).
+#pragma once
+
+#include "launch.hpp"
+#include "quantize.hpp"
+
+namespace lowbit {
+
+template <int BITS, int LOG2B, bool SR, int DT, int MODE>
+static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
+  using S = TileShape<BITS, LOG2B>;
+  const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
+  hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE>), dim3(grid_for_tiles(ntiles)),
+                     dim3(kBlockThreads), 0, s, a);
+  return launch_status();
+}
+
+template <int BITS, int LOG2B, int MODE>
+static lowbit_status launch_q_rd(bool sr, int dt, const QuantArgs& a, hipStream_t s) {
+  // stochastic rounding does not apply to the 1-bit sign code
+  if (BITS == 1 || !sr) {
+    return dt == kF32 ? launch_q<BITS, LOG2B, false, kF32, MODE>(a, s)
+                      : launch_q<BITS, LOG2B, false, kBF16, MODE>(a, s);
+  }
+  return dt == kF32 ? launch_q<BITS, LOG2B, (BITS > 1), kF32, MODE>(a, s)
+                    : launch_q<BITS, LOG2B, (BITS > 1), kBF16, MODE>(a, s);
+}
+
+template <int BITS, int MODE>
+static lowbit_status launch_q_b(int log2b, bool sr, int dt, const QuantArgs& a, hipStream_t s) {
+  switch (log2b) {
+#define LOWBIT_CASE(LB) \
+  case LB:              \
+    return launch_q_rd<BITS, LB, MODE>(sr, dt, a, s);
+    LOWBIT_FOR_EACH_LOG2B(LOWBIT_CASE)
+#undef LOWBIT_CASE
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+lowbit_status LOWBIT_TU_LAUNCHER(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
+                                 hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_q_b<1, LOWBIT_TU_MODE>(log2b, sr, dt, a, s);
+    case 2: return launch_q_b<2, LOWBIT_TU_MODE>(log2b, sr, dt, a, s);
+    case 4: return launch_q_b<4, LOWBIT_TU_MODE>(log2b, sr, dt, a, s);
+    case 8: return launch_q_b<8, LOWBIT_TU_MODE>(log2b, sr, dt, a, s);
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+}  // namespace lowbit

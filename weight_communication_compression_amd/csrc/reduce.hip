@@ -1,0 +1,39 @@
+// local reduce + requantize kernels
+#include "launch.hpp"
+#include "reduce.hpp"
+
+namespace lowbit {
+
+template <int BITS, int LOG2B, bool SR>
+static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
+  using S = TileShape<BITS, LOG2B>;
+  const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
+  hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR>), dim3(grid_for_tiles(ntiles)),
+                     dim3(kBlockThreads), 0, s, a);
+  return launch_status();
+}
+
+template <int BITS>
+static lowbit_status launch_r_b(int log2b, bool sr, const ReduceArgs& a, hipStream_t s) {
+  switch (log2b) {
+#define LOWBIT_CASE(LB)                                                       \
+  case LB:                                                                    \
+    return (BITS > 1 && sr) ? launch_r<BITS, LB, (BITS > 1)>(a, s)            \
+                            : launch_r<BITS, LB, false>(a, s);
+    LOWBIT_FOR_EACH_LOG2B(LOWBIT_CASE)
+#undef LOWBIT_CASE
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+lowbit_status launch_reduce(int bits, int log2b, bool sr, const ReduceArgs& a, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_r_b<1>(log2b, sr, a, s);
+    case 2: return launch_r_b<2>(log2b, sr, a, s);
+    case 4: return launch_r_b<4>(log2b, sr, a, s);
+    case 8: return launch_r_b<8>(log2b, sr, a, s);
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+}  // namespace lowbit
