@@ -233,13 +233,27 @@ def main() -> int:
     dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
     value = full_precision_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # plain-copy reference on the same box (not part of the step): the copy
+    # kernel's rate, and its hardware byte counters when profiled
+    copy_evs = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run((lib.lowbit_copy_f32, (P(x.data_ptr()), P(y.data_ptr()), N, sh)))
+        e1.record(stream)
+        copy_evs.append((e0, e1))
+    torch.cuda.synchronize()
+    copy_ms = sorted(e0.elapsed_time(e1) for e0, e1 in copy_evs)[2]
+    copy_gbs = 2 * N * 4 / (copy_ms * 1e-3) / 1e9
+
     name, kname, alg_bytes, _ = stages[dom]
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(kname)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname, "stage": name,
-                "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes}
+                "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes,
+                "copy_kernel_GBps": round(copy_gbs, 1)}
     kernels = {s[0]: {"us": round(per_stage[i] * 1e3, 2),
                       "alg_GBps": round(s[2] / (per_stage[i] * 1e-3) / 1e9, 1),
                       "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}

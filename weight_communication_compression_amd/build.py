@@ -35,8 +35,8 @@ HIPFLAGS = [
 ]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -44,25 +44,29 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(force: bool = True, extra: list[str] | None = None, jobs: int | None = None) -> str:
-    """Compile every HIP translation unit for gfx950 and link liblowbit.so."""
+def build(force: bool = True, extra: list[str] | None = None, jobs: int | None = None,
+          out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every HIP translation unit for gfx950 and link liblowbit.so.
+
+    `extra` adds compiler flags (e.g. -D tuning macros); `out` and `build_dir`
+    place a variant build elsewhere."""
     extra = list(extra or [])
-    os.makedirs(BUILD, exist_ok=True)
-    if not force and os.path.exists(LIB):
+    os.makedirs(build_dir, exist_ok=True)
+    if not force and os.path.exists(out):
         newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in os.listdir(CSRC))
         newest = max(newest, os.path.getmtime(os.path.join(ROOT, "include", "lowbit.h")))
-        if os.path.getmtime(LIB) >= newest:
-            return LIB
+        if os.path.getmtime(out) >= newest:
+            return out
     jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -6,10 +6,10 @@ namespace lowbit {
 
 template <int BITS, int APPLY, int DT>
 static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
-  constexpr int E = Grid<BITS>::E;
-  const int64_t nwords = (a.n + E - 1) / E;
-  const int64_t ntiles = (nwords + kWave * kDequantRows - 1) / (kWave * kDequantRows);
-  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles(ntiles)),
+  constexpr int ROWS = dequant_rows<APPLY>();
+  const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
+  const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
+  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles(ntrips)),
                      dim3(kBlockThreads), 0, s, a);
   return launch_status();
 }
@@ -32,8 +32,9 @@ lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a,
 
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
   const int64_t nvec = n / 4;
-  int64_t blocks = (nvec + 2 * kBlockThreads - 1) / (2 * kBlockThreads);
-  const int64_t cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
+  int64_t blocks = (nvec + kCopyUnroll * kBlockThreads - 1) / (kCopyUnroll * kBlockThreads);
+  int64_t cap = (int64_t)1 << 30;
+  if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, x, y, n);

@@ -1,7 +1,12 @@
 // dequant.hpp -- decompress kernels: codes + scales -> binary32, and the
-// weight-difference apply w_out = to_dtype(w_old + deq).  Lane l decodes word
-// r*64 + l of a tile of R rows; a word never straddles a block (B >= 32 >= E),
-// so each word needs one scale.
+// weight-difference apply w_out = to_dtype(w_old + deq).
+//
+// Element-centric layout: a "row" is 256 consecutive elements and lane l of a
+// wave decodes elements 4l .. 4l+3 of it, so every binary32 (or bfloat16)
+// store of the wave is one fully coalesced 1 KiB (512 B) access at any
+// bitwidth.  The 4 codes of a lane are 4b consecutive bits of one packed word
+// (lanes sharing a word read the same address, served by the cache), and a
+// word never straddles a block (B >= 32), so each lane needs one scale.
 #pragma once
 
 #include "args.hpp"
@@ -9,21 +14,32 @@
 
 namespace lowbit {
 
-constexpr int kDequantRows = 2;   // words per lane per loop trip
+// rows per lane per loop trip: decompress writes 16 B per row and lane,
+// apply also reads 8-16 B, so it keeps fewer rows in flight
+#ifndef LOWBIT_DEQ_ROWS
+#define LOWBIT_DEQ_ROWS 8
+#endif
+#ifndef LOWBIT_APPLY_ROWS
+#define LOWBIT_APPLY_ROWS 2
+#endif
+template <int APPLY>
+constexpr int dequant_rows() { return APPLY ? LOWBIT_APPLY_ROWS : LOWBIT_DEQ_ROWS; }
+constexpr int kDeqRow = kWave * 4;              // elements per row
 
+// Decode the 4 codes in bits [off, off + 4b) of `word` with scale s.
 template <int BITS>
-__device__ __forceinline__ void decode_word(uint32_t word, float s, float* d) {
+__device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* d) {
   using G = Grid<BITS>;
-  constexpr int E = G::E;
+  const uint32_t piece = word >> off;
   if constexpr (BITS == 1) {
 #pragma unroll
-    for (int j = 0; j < E; ++j) d[j] = ((word >> j) & 1u) ? s : -s;
+    for (int j = 0; j < 4; ++j) d[j] = ((piece >> j) & 1u) ? s : -s;
   } else {
-    const uint32_t tw = word ^ G::FLIP;
+    const uint32_t tw = piece ^ G::FLIP;        // fields become two's-complement q
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int q = (int)(tw << (32 - BITS * (j + 1))) >> (32 - BITS);
-      d[j] = (float)q * s;            // exact
+      d[j] = (float)q * s;                      // exact
     }
   }
 }
@@ -31,79 +47,70 @@ __device__ __forceinline__ void decode_word(uint32_t word, float s, float* d) {
 // APPLY: 0 = decompress to binary32; 1 = weight-difference apply.
 template <int BITS, int APPLY, int DT>
 __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
-  constexpr int E = Grid<BITS>::E;
-  constexpr int TILE_W = kWave * kDequantRows;             // words per tile
+  constexpr int E = Grid<BITS>::E;              // codes per word
+  constexpr int kDequantRows = dequant_rows<APPLY>();
   const int lane = lane_id();
   const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n = a.n;
-  const int64_t nwords = (n + E - 1) / E;
-  const int64_t ntiles = (nwords + TILE_W - 1) / TILE_W;
+  const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
 
-  for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t wt0 = tile * TILE_W;
-    const bool full = (wt0 + TILE_W) * E <= n;
+  for (int64_t base = wave * kDequantRows; base < nrows; base += nwaves * kDequantRows) {
     uint32_t word[kDequantRows];
     uint32_t s16[kDequantRows];
+    float wo[kDequantRows][4];
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t w = wt0 + r * kWave + lane;
+      const int64_t e0 = (base + r) * kDeqRow + 4 * lane;     // first element of this lane
       word[r] = 0;
       s16[r] = 0;
-      if (full || w < nwords) {
-        word[r] = a.codes[w];
-        s16[r] = a.scales[(w * E) >> a.log2b];
-      }
-    }
-    float wo[kDequantRows][E];
-    if constexpr (APPLY) {
-#pragma unroll
-      for (int r = 0; r < kDequantRows; ++r) {
-        const int64_t i0 = (wt0 + r * kWave + lane) * E;
-        if (full) load_vec<DT, E>(a.w_old, i0, wo[r]);
-        else load_tail<DT, E>(a.w_old, i0, n, wo[r]);
+      if (e0 < n) {
+        word[r] = a.codes[e0 / E];
+        s16[r] = a.scales[e0 >> a.log2b];
+        if constexpr (APPLY) {
+          if (e0 + 4 <= n) load_vec<DT, 4>(a.w_old, e0, wo[r]);
+          else load_tail<DT, 4>(a.w_old, e0, n, wo[r]);
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t i0 = (wt0 + r * kWave + lane) * E;
-      float d[E];
-      decode_word<BITS>(word[r], f16_bits_to_f32(s16[r]), d);
+      const int64_t e0 = (base + r) * kDeqRow + 4 * lane;
+      if (e0 >= n) continue;
+      float d[4];
+      decode4<BITS>(word[r], (int)(e0 % E) * BITS, f16_bits_to_f32(s16[r]), d);
+      const bool full = e0 + 4 <= n;
       if constexpr (!APPLY) {
-        if (full) store_vec_f32<E>(a.y, i0, d);
-        else store_tail_f32<E>(a.y, i0, n, d);
+        if (full) store_vec_f32<4>(a.y, e0, d);
+        else store_tail_f32<4>(a.y, e0, n, d);
       } else {
-        float w[E];
+        float w[4];
 #pragma unroll
-        for (int j = 0; j < E; ++j) w[j] = wo[r][j] + d[j];
+        for (int j = 0; j < 4; ++j) w[j] = wo[r][j] + d[j];
         if constexpr (DT == kF32) {
-          if (full) store_vec_f32<E>(static_cast<float*>(a.w_out), i0, w);
-          else store_tail_f32<E>(static_cast<float*>(a.w_out), i0, n, w);
+          if (full) store_vec_f32<4>(static_cast<float*>(a.w_out), e0, w);
+          else store_tail_f32<4>(static_cast<float*>(a.w_out), e0, n, w);
         } else {
-          uint16_t* out = static_cast<uint16_t*>(a.w_out) + i0;
+          uint16_t* out = static_cast<uint16_t*>(a.w_out) + e0;
           if (full) {
-            uint32_t pk[E / 2];
-#pragma unroll
-            for (int k = 0; k < E / 2; ++k)
-              pk[k] = f32_to_bf16_rne(w[2 * k]) | (f32_to_bf16_rne(w[2 * k + 1]) << 16);
-            if constexpr (E == 4) {
-              *reinterpret_cast<uint2*>(out) = make_uint2(pk[0], pk[1]);
-            } else {
-#pragma unroll
-              for (int k = 0; k < E / 8; ++k)
-                reinterpret_cast<uint4*>(out)[k] =
-                    make_uint4(pk[4 * k], pk[4 * k + 1], pk[4 * k + 2], pk[4 * k + 3]);
-            }
+            *reinterpret_cast<uint2*>(out) =
+                make_uint2(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16),
+                           f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16));
           } else {
 #pragma unroll
-            for (int j = 0; j < E; ++j)
-              if (i0 + j < n) out[j] = (uint16_t)f32_to_bf16_rne(w[j]);
+            for (int j = 0; j < 4; ++j)
+              if (e0 + j < n) out[j] = (uint16_t)f32_to_bf16_rne(w[j]);
           }
         }
       }
     }
   }
 }
+
+#ifndef LOWBIT_COPY_UNROLL
+#define LOWBIT_COPY_UNROLL 1
+#endif
+constexpr int kCopyUnroll = LOWBIT_COPY_UNROLL;
 
 // Plain binary32 copy with the codec kernels' launch shape (measurement aid).
 __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, float* y, int64_t n) {
@@ -112,13 +119,14 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, flo
   const float4* xv = reinterpret_cast<const float4*>(x);
   float4* yv = reinterpret_cast<float4*>(y);
   int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-  for (; i + stride < nvec; i += 2 * stride) {
-    float4 a = xv[i];
-    float4 b = xv[i + stride];
-    yv[i] = a;
-    yv[i + stride] = b;
+  for (; i + (kCopyUnroll - 1) * stride < nvec; i += kCopyUnroll * stride) {
+    float4 t[kCopyUnroll];
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) t[k] = xv[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) yv[i + k * stride] = t[k];
   }
-  if (i < nvec) yv[i] = xv[i];
+  for (; i < nvec; i += stride) yv[i] = xv[i];
   const int64_t t = nvec * 4 + (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (t < n) y[t] = x[t];
 }

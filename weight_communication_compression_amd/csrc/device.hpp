@@ -41,6 +41,17 @@ struct Grid {
   }();
 };
 
+#ifndef LOWBIT_ELEMS_PER_TRIP
+#define LOWBIT_ELEMS_PER_TRIP 8    // per-lane elements a wave loads per loop trip
+#endif
+
+// Tiles per loop trip for a kernel whose tile gives each lane PER_LANE
+// elements: enough to keep LOWBIT_ELEMS_PER_TRIP elements per lane in flight.
+template <int PER_LANE>
+constexpr int tiles_per_trip() {
+  return PER_LANE >= LOWBIT_ELEMS_PER_TRIP ? 1 : LOWBIT_ELEMS_PER_TRIP / PER_LANE;
+}
+
 // ---------------------------------------------------------------- lanes --
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -76,6 +87,29 @@ __device__ __forceinline__ float group_reduce(float v) {
   if constexpr (L >= 32) v = op(v, swizzle_f32<0x401F>(v));  // lane ^ 16 within 32
   if constexpr (L >= 64) v = op(readlane_f32(v, 0), readlane_f32(v, 32));
   return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum over aligned groups of L lanes of a non-negative binary32 value,
+// taken on the bit patterns: for non-negative floats the unsigned integer
+// order is the numeric order, and v_max_u32 folds the DPP move into itself.
+template <int L>
+__device__ __forceinline__ float group_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  if constexpr (L >= 2) v = max(v, dpp_u32<0xB1>(v));
+  if constexpr (L >= 4) v = max(v, dpp_u32<0x4E>(v));
+  if constexpr (L >= 8) v = max(v, dpp_u32<0x141>(v));
+  if constexpr (L >= 16) v = max(v, dpp_u32<0x140>(v));
+  if constexpr (L >= 32)
+    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if constexpr (L >= 64)
+    v = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+            (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  return __uint_as_float(v);
 }
 
 // Adjacent-pairs tree sum of |v[0..N)| within one lane (N a power of two).
@@ -128,13 +162,38 @@ struct BlockScale {
   float inv;      // fl(1 / s), or 0 when s == 0
 };
 
-// t = fl(stat / div); s16 = round-up binary16 of t.
-__device__ __forceinline__ BlockScale make_scale(float stat, float div) {
+// fl(a / Q) for a >= 0: one multiply by fl(1/Q) and one FMA correction.
+// Equal to the IEEE quotient for every non-negative finite binary32 a and
+// Q in {7, 127} (checked exhaustively on the CPU by the test suite).
+template <int Q>
+__device__ __forceinline__ float div_by_grid(float a) {
+  if constexpr (Q == 1) {
+    return a;
+  } else {
+    constexpr float c = 1.0f / (float)Q;
+    const float q0 = a * c;
+    const float r = __builtin_fmaf(-q0, (float)Q, a);
+    return __builtin_fmaf(r, c, q0);
+  }
+}
+
+// fl(1 / s) for a binary16 value s >= 0 (0 -> 0).  s has an 11-bit
+// significand, so 1/s lies at least 2^-12 ulp from any rounding midpoint, and
+// one FMA Newton step from the hardware estimate (within 1 ulp) rounds
+// correctly (checked for every binary16 s and every estimate within 2 ulp).
+__device__ __forceinline__ float recip_f16_value(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  const float y1 = __builtin_fmaf(e, y0, y0);
+  return s != 0.0f ? y1 : 0.0f;
+}
+
+// s16 = round-up binary16 of t, its value and reciprocal.
+__device__ __forceinline__ BlockScale make_scale(float t) {
   BlockScale r;
-  float t = stat / div;                       // correctly rounded division
   r.s16 = f16_round_up(t);
   r.s = f16_bits_to_f32(r.s16);
-  r.inv = (r.s != 0.0f) ? 1.0f / r.s : 0.0f;  // correctly rounded division
+  r.inv = recip_f16_value(r.s);
   return r;
 }
 

@@ -8,8 +8,13 @@
 #include "../../include/lowbit.h"
 #include "args.hpp"
 
+// Optional cap on the grid, in workgroups per CU (0: no cap).  Without a cap
+// every wave makes one trip through its kernel's loop: on MI355X a grid that
+// walks memory once, in order, sustains far more HBM bandwidth than a
+// persistent grid-stride loop (measured: 6.8 vs 5-6 TB/s reads, 6.9 vs
+// 4.3-5.1 TB/s writes).
 #ifndef LOWBIT_BLOCKS_PER_CU
-#define LOWBIT_BLOCKS_PER_CU 8     // 256-thread workgroups resident per CU at most
+#define LOWBIT_BLOCKS_PER_CU 0
 #endif
 
 namespace lowbit {
@@ -18,12 +23,14 @@ namespace lowbit {
 // Number of compute units of the current device (cached per device id).
 int device_cu_count();
 
-// Grid for a wave-per-tile kernel: one wave per tile, at most
-// LOWBIT_BLOCKS_PER_CU workgroups per CU; the kernels loop over the rest.
-inline int grid_for_tiles(int64_t ntiles) {
+// Grid for a kernel where each wave takes `ntrips` trips' worth of work: one
+// wave per trip (4 per workgroup); the kernels loop over whatever a cap
+// leaves.  The grid stays below 2^31 workgroups.
+inline int grid_for_tiles(int64_t ntrips) {
   const int64_t waves_per_block = 256 / 64;
-  int64_t blocks = (ntiles + waves_per_block - 1) / waves_per_block;
-  const int64_t cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
+  int64_t blocks = (ntrips + waves_per_block - 1) / waves_per_block;
+  int64_t cap = (int64_t)1 << 30;
+  if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return (int)blocks;

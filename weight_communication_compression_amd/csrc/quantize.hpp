@@ -45,24 +45,28 @@ __device__ __forceinline__ void quantize_tile(
 
   // ---- block statistic and scale ----------------------------------------
   const int64_t blk0 = (R == 1) ? t0 + (int64_t)(lane / L) * B : t0;   // block's first element
-  float stat, div;
+  float t;   // fl(statistic / divisor)
   if constexpr (BITS == 1) {
     float g[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) g[r] = group_reduce<L, true>(lane_abs_tree<E>(v[r]));
-    stat = reg_tree<R>(g);
-    const int64_t rem = n - blk0;
-    div = (float)(rem < B ? rem : B);      // valid elements of the block
+    const float S = reg_tree<R>(g);
+    // mean over the valid elements; for a full block the divisor is the
+    // power of two B and the multiply by 1/B is exact
+    t = S * (1.0f / (float)B);
+    if (!full) {
+      const int64_t rem = n - blk0;
+      if (rem < B) t = S / (float)rem;
+    }
   } else {
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[r][j]));
-    stat = group_reduce<L, false>(m);
-    div = QMAX;
+    t = div_by_grid<G::QMAX>(group_max_nonneg<L>(m));
   }
-  const BlockScale sc = make_scale(stat, div);
+  const BlockScale sc = make_scale(t);
   if ((lane & (L - 1)) == 0 && blk0 < n) o.scales[blk0 >> LOG2B] = (uint16_t)sc.s16;
 
   // ---- codes and packing ---------------------------------------------------
@@ -118,10 +122,14 @@ __device__ __forceinline__ void quantize_tile(
   }
 }
 
+// Each wave handles U consecutive tiles per loop trip: all of their loads are
+// issued before any of them is quantized, so a wave keeps U tiles of HBM
+// reads in flight while it computes.
 template <int BITS, int LOG2B, bool SR, int DT, int MODE>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
+  constexpr int U = tiles_per_trip<R * E>();
   constexpr bool EF = MODE == kErrorFeedback;
 
   const int lane = lane_id();
@@ -130,46 +138,54 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a) {
   const int64_t n = a.n;
   const int64_t ntiles = (n + S::TILE - 1) / S::TILE;
 
-  for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t t0 = tile * S::TILE;
-    const bool full = t0 + S::TILE <= n;   // wave-uniform
-
-    float v[R][E];
+  for (int64_t base = wave * U; base < ntiles; base += nwaves * U) {
+    float v[U][R][E];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t i0 = t0 + (int64_t)(r * kWave + lane) * E;
-      float w[E];
-      if (full) {
-        load_vec<DT, E>(a.x, i0, v[r]);
-        if constexpr (MODE == kErrorFeedback) load_vec<kF32, E>(a.resid, i0, w);
-        if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, i0, w);
-      } else {
-        load_tail<DT, E>(a.x, i0, n, v[r]);
-        if constexpr (MODE == kErrorFeedback) load_tail<kF32, E>(a.resid, i0, n, w);
-        if constexpr (MODE == kWeightDiff) load_tail<DT, E>(a.x2, i0, n, w);
-      }
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        if constexpr (MODE == kErrorFeedback) v[r][j] = v[r][j] + w[j];   // a = g + e
-        if constexpr (MODE == kWeightDiff) v[r][j] = v[r][j] - w[j];      // d = w_new - w_old
-      }
-    }
-
-    float deq[R][E];
-    quantize_tile<BITS, LOG2B, SR, EF>(v, t0, n, full, a.out, deq);
-
-    if constexpr (EF) {
+    for (int u = 0; u < U; ++u) {
+      const int64_t t0 = (base + u) * S::TILE;
+      if (base + u >= ntiles) break;                 // wave-uniform
+      const bool full = t0 + S::TILE <= n;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int64_t i0 = t0 + (int64_t)(r * kWave + lane) * E;
-        float e[E];
+        float w[E];
+        if (full) {
+          load_vec<DT, E>(a.x, i0, v[u][r]);
+          if constexpr (MODE == kErrorFeedback) load_vec<kF32, E>(a.resid, i0, w);
+          if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, i0, w);
+        } else {
+          load_tail<DT, E>(a.x, i0, n, v[u][r]);
+          if constexpr (MODE == kErrorFeedback) load_tail<kF32, E>(a.resid, i0, n, w);
+          if constexpr (MODE == kWeightDiff) load_tail<DT, E>(a.x2, i0, n, w);
+        }
 #pragma unroll
-        for (int j = 0; j < E; ++j) e[j] = v[r][j] - deq[r][j];          // e = a - deq
-        if (full) store_vec_f32<E>(a.resid, i0, e);
-        else store_tail_f32<E>(a.resid, i0, n, e);
+        for (int j = 0; j < E; ++j) {
+          if constexpr (MODE == kErrorFeedback) v[u][r][j] = v[u][r][j] + w[j];  // a = g + e
+          if constexpr (MODE == kWeightDiff) v[u][r][j] = v[u][r][j] - w[j];     // w_new - w_old
+        }
       }
     }
-    (void)deq;
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t0 = (base + u) * S::TILE;
+      if (base + u >= ntiles) break;
+      const bool full = t0 + S::TILE <= n;
+      float deq[R][E];
+      quantize_tile<BITS, LOG2B, SR, EF>(v[u], t0, n, full, a.out, deq);
+      if constexpr (EF) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t i0 = t0 + (int64_t)(r * kWave + lane) * E;
+          float e[E];
+#pragma unroll
+          for (int j = 0; j < E; ++j) e[j] = v[u][r][j] - deq[r][j];     // e = a - deq
+          if (full) store_vec_f32<E>(a.resid, i0, e);
+          else store_tail_f32<E>(a.resid, i0, n, e);
+        }
+      }
+      (void)deq;
+    }
   }
 }
 

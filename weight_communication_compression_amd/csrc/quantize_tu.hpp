@@ -11,8 +11,10 @@ namespace lowbit {
 template <int BITS, int LOG2B, bool SR, int DT, int MODE>
 static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
   using S = TileShape<BITS, LOG2B>;
+  constexpr int U = tiles_per_trip<S::R * S::E>();
   const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
-  hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE>), dim3(grid_for_tiles(ntiles)),
+  hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE>),
+                     dim3(grid_for_tiles((ntiles + U - 1) / U)),
                      dim3(kBlockThreads), 0, s, a);
   return launch_status();
 }

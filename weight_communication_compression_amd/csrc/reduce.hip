@@ -7,8 +7,9 @@ namespace lowbit {
 template <int BITS, int LOG2B, bool SR>
 static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
   using S = TileShape<BITS, LOG2B>;
+  constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
   const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
-  hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR>), dim3(grid_for_tiles(ntiles)),
+  hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR>), dim3(grid_for_tiles((ntiles + U - 1) / U)),
                      dim3(kBlockThreads), 0, s, a);
   return launch_status();
 }
