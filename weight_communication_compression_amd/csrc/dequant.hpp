@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
   constexpr int E = Grid<BITS>::E;              // codes per word
   constexpr int kDequantRows = dequant_rows<APPLY>();
   const int lane = lane_id();
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x >> 6);
+  const int64_t wave = global_wave_id();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n = a.n;
   const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
@@ -59,39 +59,43 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
     uint32_t word[kDequantRows];
     uint32_t s16[kDequantRows];
     float wo[kDequantRows][4];
+    const uint32_t lo = 4u * (uint32_t)lane;                  // lane's element within a row
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t e0 = (base + r) * kDeqRow + 4 * lane;     // first element of this lane
+      const int64_t r0 = (base + r) * kDeqRow;                // row start (wave-uniform)
       word[r] = 0;
       s16[r] = 0;
-      if (e0 < n) {
-        word[r] = a.codes[e0 / E];
-        s16[r] = a.scales[e0 >> a.log2b];
+      if (r0 + lo < n) {
+        word[r] = (a.codes + r0 / E)[lo / E];
+        // blocks of >= 256 elements cover the whole row: one scale per row
+        s16[r] = a.log2b >= 8 ? a.scales[r0 >> a.log2b]
+                              : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
         if constexpr (APPLY) {
-          if (e0 + 4 <= n) load_vec<DT, 4>(a.w_old, e0, wo[r]);
-          else load_tail<DT, 4>(a.w_old, e0, n, wo[r]);
+          if (r0 + lo + 4 <= n) load_vec<DT, 4>(a.w_old, r0, lo, wo[r]);
+          else load_tail<DT, 4>(a.w_old, r0, lo, n - r0, wo[r]);
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t e0 = (base + r) * kDeqRow + 4 * lane;
-      if (e0 >= n) continue;
+      const int64_t r0 = (base + r) * kDeqRow;
+      if (r0 + lo >= n) continue;
       float d[4];
-      decode4<BITS>(word[r], (int)(e0 % E) * BITS, f16_bits_to_f32(s16[r]), d);
-      const bool full = e0 + 4 <= n;
+      decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d);
+      const bool full = r0 + lo + 4 <= n;
       if constexpr (!APPLY) {
-        if (full) store_vec_f32<4>(a.y, e0, d);
-        else store_tail_f32<4>(a.y, e0, n, d);
+        if (full) store_vec_f32<4>(a.y, r0, lo, d);
+        else store_tail_f32<4>(a.y, r0, lo, n - r0, d);
       } else {
         float w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = wo[r][j] + d[j];
         if constexpr (DT == kF32) {
-          if (full) store_vec_f32<4>(static_cast<float*>(a.w_out), e0, w);
-          else store_tail_f32<4>(static_cast<float*>(a.w_out), e0, n, w);
+          if (full) store_vec_f32<4>(static_cast<float*>(a.w_out), r0, lo, w);
+          else store_tail_f32<4>(static_cast<float*>(a.w_out), r0, lo, n - r0, w);
         } else {
-          uint16_t* out = static_cast<uint16_t*>(a.w_out) + e0;
+          const int64_t e0 = r0 + lo;
+          uint16_t* out = static_cast<uint16_t*>(a.w_out) + r0 + lo;
           if (full) {
             *reinterpret_cast<uint2*>(out) =
                 make_uint2(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16),

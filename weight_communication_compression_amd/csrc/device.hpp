@@ -12,7 +12,14 @@
 namespace lowbit {
 
 constexpr int kWave = 64;
-constexpr int kBlockThreads = 256;              // 4 waves per workgroup
+#ifndef LOWBIT_BLOCK_THREADS
+#define LOWBIT_BLOCK_THREADS 256
+#endif
+constexpr int kBlockThreads = LOWBIT_BLOCK_THREADS;   // threads per workgroup
+#ifndef LOWBIT_XCD_REMAP
+#define LOWBIT_XCD_REMAP 0
+#endif
+constexpr int kXcds = 8;                              // MI355X: 8 XCDs of 32 CUs
 constexpr float kMagic = 12582912.0f;           // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;    // bit pattern of kMagic
 
@@ -41,19 +48,52 @@ struct Grid {
   }();
 };
 
+// Per-lane elements a wave loads per loop trip: nearest rounding is light on
+// ALU and prefers short trips; stochastic rounding hides its hashing better
+// with a second tile's loads in flight.
 #ifndef LOWBIT_ELEMS_PER_TRIP
-#define LOWBIT_ELEMS_PER_TRIP 8    // per-lane elements a wave loads per loop trip
+#define LOWBIT_ELEMS_PER_TRIP 8
+#endif
+#ifndef LOWBIT_SR_ELEMS_PER_TRIP
+#define LOWBIT_SR_ELEMS_PER_TRIP 16
 #endif
 
 // Tiles per loop trip for a kernel whose tile gives each lane PER_LANE
-// elements: enough to keep LOWBIT_ELEMS_PER_TRIP elements per lane in flight.
-template <int PER_LANE>
+// elements.
+template <int PER_LANE, bool SR = false>
 constexpr int tiles_per_trip() {
-  return PER_LANE >= LOWBIT_ELEMS_PER_TRIP ? 1 : LOWBIT_ELEMS_PER_TRIP / PER_LANE;
+  constexpr int want = SR ? LOWBIT_SR_ELEMS_PER_TRIP : LOWBIT_ELEMS_PER_TRIP;
+  return PER_LANE >= want ? 1 : want / PER_LANE;
 }
+
+// Non-temporal hint on the large binary32 outputs (decompressed values,
+// residuals, sums, applied weights): written through rather than parked dirty
+// in the Infinity Cache, where the next kernel would pay for their write-back
+// (measured: +12 % on a whole compress/reduce/decompress/EF/weight-diff pass).
+#ifndef LOWBIT_NT_STORES
+#define LOWBIT_NT_STORES 1
+#endif
 
 // ---------------------------------------------------------------- lanes --
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Index of this wave in the grid, as a wave-uniform (scalar) value: element
+// offsets then split into a scalar base and a 32-bit per-lane offset, and
+// loads and stores use the scalar-base addressing mode.
+__device__ __forceinline__ int64_t global_wave_id() {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int64_t b = blockIdx.x;
+  if (LOWBIT_XCD_REMAP) {
+    // workgroups are dealt to the XCDs round-robin (b % 8); give each XCD one
+    // contiguous range of the work instead, so neighbouring tiles (and the
+    // cache lines of codes and scales they share) stay in one L2
+    const int64_t nb = gridDim.x;
+    const int64_t q = nb / kXcds, r = nb % kXcds;
+    const int64_t x = b % kXcds, i = b / kXcds;
+    b = x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+  }
+  return b * (kBlockThreads / kWave) + w;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -212,33 +252,39 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Load E consecutive elements starting at element i0 (16-byte aligned for
-// E >= 8 in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16).
+// Element access helpers.  Every address is split into the buffer base plus
+// a wave-uniform element offset t0 (scalar registers) and a 32-bit per-lane
+// element offset `off`, which maps onto the scalar-base + 32-bit-offset
+// addressing mode of global loads and stores.
+
+// Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
+// in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16).
 template <int DT, int E>
-__device__ __forceinline__ void load_vec(const void* base, int64_t i0, float* v) {
+__device__ __forceinline__ void load_vec(const void* base, int64_t t0, uint32_t off, float* v) {
   if constexpr (DT == kF32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i0);
+    const float* p = static_cast<const float*>(base) + t0;
+    const float4* q = reinterpret_cast<const float4*>(p + off);
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-      float4 t = p[k];
+      float4 t = q[k];
       v[4 * k + 0] = t.x;
       v[4 * k + 1] = t.y;
       v[4 * k + 2] = t.z;
       v[4 * k + 3] = t.w;
     }
   } else {
-    const uint16_t* b = static_cast<const uint16_t*>(base) + i0;
+    const uint16_t* p = static_cast<const uint16_t*>(base) + t0;
     if constexpr (E == 4) {
-      uint2 t = *reinterpret_cast<const uint2*>(b);
+      uint2 t = *reinterpret_cast<const uint2*>(p + off);
       v[0] = bf16_lo(t.x);
       v[1] = bf16_hi(t.x);
       v[2] = bf16_lo(t.y);
       v[3] = bf16_hi(t.y);
     } else {
-      const uint4* p = reinterpret_cast<const uint4*>(b);
+      const uint4* q = reinterpret_cast<const uint4*>(p + off);
 #pragma unroll
       for (int k = 0; k < E / 8; ++k) {
-        uint4 t = p[k];
+        uint4 t = q[k];
         v[8 * k + 0] = bf16_lo(t.x);
         v[8 * k + 1] = bf16_hi(t.x);
         v[8 * k + 2] = bf16_lo(t.y);
@@ -252,34 +298,44 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t i0, float* v)
   }
 }
 
-// Guarded element-by-element load for the ragged last tile: positions at or
-// past n read as +0.
+// Guarded element-by-element load for a ragged last tile: positions
+// off + j >= rem (rem = n - t0, the valid elements from t0 on) read as +0.
 template <int DT, int E>
-__device__ __forceinline__ void load_tail(const void* base, int64_t i0, int64_t n, float* v) {
+__device__ __forceinline__ void load_tail(const void* base, int64_t t0, uint32_t off, int64_t rem,
+                                          float* v) {
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    int64_t i = i0 + j;
     float x = 0.0f;
-    if (i < n) {
-      if constexpr (DT == kF32) x = static_cast<const float*>(base)[i];
-      else x = __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+    if ((int64_t)off + j < rem) {
+      if constexpr (DT == kF32) x = (static_cast<const float*>(base) + t0)[off + j];
+      else x = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(base) + t0)[off + j] << 16);
     }
     v[j] = x;
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int E>
-__device__ __forceinline__ void store_vec_f32(float* base, int64_t i0, const float* v) {
-  float4* p = reinterpret_cast<float4*>(base + i0);
+__device__ __forceinline__ void store_vec_f32(float* base, int64_t t0, uint32_t off, const float* v) {
+  float* p = base + t0 + off;
 #pragma unroll
-  for (int k = 0; k < E / 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  for (int k = 0; k < E / 4; ++k) {
+    if (LOWBIT_NT_STORES) {
+      const f32x4 q = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+      __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(p) + k);
+    } else {
+      reinterpret_cast<float4*>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    }
+  }
 }
 
 template <int E>
-__device__ __forceinline__ void store_tail_f32(float* base, int64_t i0, int64_t n, const float* v) {
+__device__ __forceinline__ void store_tail_f32(float* base, int64_t t0, uint32_t off, int64_t rem,
+                                               const float* v) {
 #pragma unroll
   for (int j = 0; j < E; ++j)
-    if (i0 + j < n) base[i0 + j] = v[j];
+    if ((int64_t)off + j < rem) (base + t0)[off + j] = v[j];
 }
 
 // binary32 -> bfloat16, round to nearest even, by integer arithmetic.

@@ -7,6 +7,7 @@
 
 #include "../../include/lowbit.h"
 #include "args.hpp"
+#include "device.hpp"
 
 // Optional cap on the grid, in workgroups per CU (0: no cap).  Without a cap
 // every wave makes one trip through its kernel's loop: on MI355X a grid that
@@ -27,7 +28,7 @@ int device_cu_count();
 // wave per trip (4 per workgroup); the kernels loop over whatever a cap
 // leaves.  The grid stays below 2^31 workgroups.
 inline int grid_for_tiles(int64_t ntrips) {
-  const int64_t waves_per_block = 256 / 64;
+  const int64_t waves_per_block = kBlockThreads / kWave;
   int64_t blocks = (ntrips + waves_per_block - 1) / waves_per_block;
   int64_t cap = (int64_t)1 << 30;
   if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;

@@ -30,10 +30,13 @@ struct TileShape {
   static constexpr int L = B > ROW ? kWave : B / E;      // lanes per block
 };
 
-// Quantize the tile starting at element t0 whose values are v[r][j] (element
-// t0 + (r*64 + lane)*E + j; positions at or past n must hold +0).  Stores the
-// codes and scales; when WANT_DEQ, deq[r][j] receives the dequantized values.
-template <int BITS, int LOG2B, bool SR, bool WANT_DEQ>
+// Quantize the tile starting at element t0 whose values are 2^-K * v[r][j]
+// (element t0 + (r*64 + lane)*E + j; positions at or past n must hold +0).
+// Stores the codes and scales; when WANT_DEQ, deq[r][j] receives the
+// dequantized values.  K > 0 lets a caller hand over values it accumulated
+// scaled by 2^K: the statistic and the reciprocal absorb the exact factor, so
+// the codes are those of the unscaled values (no value here is subnormal).
+template <int BITS, int LOG2B, bool SR, bool WANT_DEQ, int K = 0>
 __device__ __forceinline__ void quantize_tile(
     const float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E], int64_t t0, int64_t n,
     bool full, const TileOut& o, float (&deq)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
@@ -41,7 +44,22 @@ __device__ __forceinline__ void quantize_tile(
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R, L = S::L, B = S::B;
   constexpr float QMAX = (float)G::QMAX;
+  constexpr float UNSCALE = 1.0f / (float)(1 << K);       // exact power of two
+  static_assert(K == 0 || BITS > 1, "scaled input is only for the max statistic");
   const int lane = lane_id();
+
+  // ---- 1 bit: the codes are the signs and need no scale; take them first so
+  // that the values are only needed by the sum tree afterwards
+  uint32_t sign_word[R];
+  if constexpr (BITS == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j) w |= (v[r][j] >= 0.0f ? 1u : 0u) << j;
+      sign_word[r] = w;
+    }
+  }
 
   // ---- block statistic and scale ----------------------------------------
   const int64_t blk0 = (R == 1) ? t0 + (int64_t)(lane / L) * B : t0;   // block's first element
@@ -64,24 +82,25 @@ __device__ __forceinline__ void quantize_tile(
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[r][j]));
-    t = div_by_grid<G::QMAX>(group_max_nonneg<L>(m));
+    t = div_by_grid<G::QMAX>(group_max_nonneg<L>(m) * UNSCALE);
   }
   const BlockScale sc = make_scale(t);
-  if ((lane & (L - 1)) == 0 && blk0 < n) o.scales[blk0 >> LOG2B] = (uint16_t)sc.s16;
+  const float inv = sc.inv * UNSCALE;
+  if ((lane & (L - 1)) == 0 && blk0 < n)
+    (o.scales + (t0 >> LOG2B))[R == 1 ? lane / L : 0] = (uint16_t)sc.s16;
 
   // ---- codes and packing ---------------------------------------------------
+  uint32_t* const cbase = o.codes + t0 / E;           // the tile's first word
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t w0 = t0 / E + r * kWave + lane;     // word index
-    const int64_t i0 = w0 * E;                        // its first element
+    const uint32_t wl = (uint32_t)(r * kWave + lane);  // word within the tile
+    const int64_t i0 = t0 + (int64_t)wl * E;           // its first element
     uint32_t word;
     if constexpr (BITS == 1) {
-      word = 0;
+      word = sign_word[r];
+      if constexpr (WANT_DEQ) {
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const bool pos = v[r][j] >= 0.0f;
-        word |= (pos ? 1u : 0u) << j;
-        if constexpr (WANT_DEQ) deq[r][j] = pos ? sc.s : -sc.s;
+        for (int j = 0; j < E; ++j) deq[r][j] = ((word >> j) & 1u) ? sc.s : -sc.s;
       }
     } else {
       word = G::PACK_BIAS;
@@ -93,7 +112,7 @@ __device__ __forceinline__ void quantize_tile(
       }
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        const float x = v[r][j] * sc.inv;
+        const float x = v[r][j] * inv;
         float q;
         if constexpr (SR) {
           const uint32_t h = fmix32((lo + (uint32_t)j) ^ hk);
@@ -113,78 +132,103 @@ __device__ __forceinline__ void quantize_tile(
       }
     }
     if (full) {
-      o.codes[w0] = word;
+      cbase[wl] = word;
     } else if (i0 < n) {
       const int64_t valid = n - i0;
       if (valid < E) word &= (1u << (valid * BITS)) - 1u;
-      o.codes[w0] = word;
+      cbase[wl] = word;
     }
   }
 }
 
-// Each wave handles U consecutive tiles per loop trip: all of their loads are
-// issued before any of them is quantized, so a wave keeps U tiles of HBM
-// reads in flight while it computes.
-template <int BITS, int LOG2B, bool SR, int DT, int MODE>
-__global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a) {
+// Load one tile's values (x, plus the residual or minus the old weights).
+template <int BITS, int LOG2B, int DT, int MODE, bool FULL>
+__device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
+                                          float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
-  constexpr int U = tiles_per_trip<R * E>();
-  constexpr bool EF = MODE == kErrorFeedback;
-
   const int lane = lane_id();
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t n = a.n;
-  const int64_t ntiles = (n + S::TILE - 1) / S::TILE;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t off = (uint32_t)(r * kWave + lane) * E;
+    float w[E];
+    if constexpr (FULL) {
+      load_vec<DT, E>(a.x, t0, off, v[r]);
+      if constexpr (MODE == kErrorFeedback) load_vec<kF32, E>(a.resid, t0, off, w);
+      if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, t0, off, w);
+    } else {
+      load_tail<DT, E>(a.x, t0, off, a.n - t0, v[r]);
+      if constexpr (MODE == kErrorFeedback) load_tail<kF32, E>(a.resid, t0, off, a.n - t0, w);
+      if constexpr (MODE == kWeightDiff) load_tail<DT, E>(a.x2, t0, off, a.n - t0, w);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if constexpr (MODE == kErrorFeedback) v[r][j] = v[r][j] + w[j];   // a = g + e
+      if constexpr (MODE == kWeightDiff) v[r][j] = v[r][j] - w[j];      // w_new - w_old
+    }
+  }
+}
 
-  for (int64_t base = wave * U; base < ntiles; base += nwaves * U) {
-    float v[U][R][E];
+// Quantize one loaded tile; in error-feedback mode also write e = a - deq.
+template <int BITS, int LOG2B, bool SR, int MODE, bool FULL>
+__device__ __forceinline__ void finish_tile(const QuantArgs& a, int64_t t0,
+                                            const float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R;
+  constexpr bool EF = MODE == kErrorFeedback;
+  const int lane = lane_id();
+  float deq[R][E];
+  quantize_tile<BITS, LOG2B, SR, EF>(v, t0, a.n, FULL, a.out, deq);
+  if constexpr (EF) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t0 = (base + u) * S::TILE;
-      if (base + u >= ntiles) break;                 // wave-uniform
-      const bool full = t0 + S::TILE <= n;
+    for (int r = 0; r < R; ++r) {
+      const uint32_t off = (uint32_t)(r * kWave + lane) * E;
+      float e[E];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t i0 = t0 + (int64_t)(r * kWave + lane) * E;
-        float w[E];
-        if (full) {
-          load_vec<DT, E>(a.x, i0, v[u][r]);
-          if constexpr (MODE == kErrorFeedback) load_vec<kF32, E>(a.resid, i0, w);
-          if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, i0, w);
-        } else {
-          load_tail<DT, E>(a.x, i0, n, v[u][r]);
-          if constexpr (MODE == kErrorFeedback) load_tail<kF32, E>(a.resid, i0, n, w);
-          if constexpr (MODE == kWeightDiff) load_tail<DT, E>(a.x2, i0, n, w);
-        }
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          if constexpr (MODE == kErrorFeedback) v[u][r][j] = v[u][r][j] + w[j];  // a = g + e
-          if constexpr (MODE == kWeightDiff) v[u][r][j] = v[u][r][j] - w[j];     // w_new - w_old
-        }
+      for (int j = 0; j < E; ++j) e[j] = v[r][j] - deq[r][j];          // e = a - deq
+      if constexpr (FULL) store_vec_f32<E>(a.resid, t0, off, e);
+      else store_tail_f32<E>(a.resid, t0, off, a.n - t0, e);
+    }
+  }
+  (void)deq;
+}
+
+// Main kernel (TAIL = false): each wave takes one trip of U full tiles -- all
+// of their loads are issued before any of them is quantized -- and the grid
+// covers the complete trips of full tiles only, so this code has no bounds
+// checks.  Tail kernel (TAIL = true, launched with one wave when needed):
+// the remaining tiles from tile `first`, the last of which may be partial.
+template <int BITS, int LOG2B, bool SR, int DT, int MODE, bool TAIL>
+__global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a, int64_t first) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R;
+  constexpr int U = tiles_per_trip<R * E, SR>();
+
+  if constexpr (TAIL) {
+    if (global_wave_id() != 0) return;
+    const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
+    for (int64_t tile = first; tile < ntiles; ++tile) {
+      const int64_t t0 = tile * S::TILE;
+      float v[R][E];
+      if (t0 + S::TILE <= a.n) {
+        load_tile<BITS, LOG2B, DT, MODE, true>(a, t0, v);
+        finish_tile<BITS, LOG2B, SR, MODE, true>(a, t0, v);
+      } else {
+        load_tile<BITS, LOG2B, DT, MODE, false>(a, t0, v);
+        finish_tile<BITS, LOG2B, SR, MODE, false>(a, t0, v);
       }
     }
-
+  } else {
+    const int64_t ntrips = first / U;                 // first = number of full tiles
+    const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+    for (int64_t trip = global_wave_id(); trip < ntrips; trip += nwaves) {
+      float v[U][R][E];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t0 = (base + u) * S::TILE;
-      if (base + u >= ntiles) break;
-      const bool full = t0 + S::TILE <= n;
-      float deq[R][E];
-      quantize_tile<BITS, LOG2B, SR, EF>(v[u], t0, n, full, a.out, deq);
-      if constexpr (EF) {
+      for (int u = 0; u < U; ++u)
+        load_tile<BITS, LOG2B, DT, MODE, true>(a, (trip * U + u) * S::TILE, v[u]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t i0 = t0 + (int64_t)(r * kWave + lane) * E;
-          float e[E];
-#pragma unroll
-          for (int j = 0; j < E; ++j) e[j] = v[u][r][j] - deq[r][j];     // e = a - deq
-          if (full) store_vec_f32<E>(a.resid, i0, e);
-          else store_tail_f32<E>(a.resid, i0, n, e);
-        }
-      }
-      (void)deq;
+      for (int u = 0; u < U; ++u)
+        finish_tile<BITS, LOG2B, SR, MODE, true>(a, (trip * U + u) * S::TILE, v[u]);
     }
   }
 }

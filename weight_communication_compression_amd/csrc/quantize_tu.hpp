@@ -8,14 +8,22 @@
 
 namespace lowbit {
 
+// Main kernel over the complete trips of full tiles; one-wave tail kernel for
+// whatever remains (fewer than U full tiles and a partial last tile).
 template <int BITS, int LOG2B, bool SR, int DT, int MODE>
 static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
   using S = TileShape<BITS, LOG2B>;
-  constexpr int U = tiles_per_trip<S::R * S::E>();
-  const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
-  hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE>),
-                     dim3(grid_for_tiles((ntiles + U - 1) / U)),
-                     dim3(kBlockThreads), 0, s, a);
+  constexpr int U = tiles_per_trip<S::R * S::E, SR>();
+  const int64_t full_tiles = a.n / S::TILE;
+  const int64_t ntrips = full_tiles / U;
+  if (ntrips > 0) {
+    hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, false>),
+                       dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+  }
+  if (ntrips * U * S::TILE < a.n) {
+    hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, true>), dim3(1), dim3(kWave),
+                       0, s, a, ntrips * U);
+  }
   return launch_status();
 }
 

@@ -4,13 +4,22 @@
 
 namespace lowbit {
 
+// Main kernel over the complete trips of full tiles; one-wave tail kernel for
+// whatever remains.
 template <int BITS, int LOG2B, bool SR>
 static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
-  const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
-  hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR>), dim3(grid_for_tiles((ntiles + U - 1) / U)),
-                     dim3(kBlockThreads), 0, s, a);
+  const int64_t full_tiles = a.n / S::TILE;
+  const int64_t ntrips = full_tiles / U;
+  if (ntrips > 0) {
+    hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR, false>), dim3(grid_for_tiles(ntrips)),
+                       dim3(kBlockThreads), 0, s, a, full_tiles);
+  }
+  if (ntrips * U * S::TILE < a.n) {
+    hipLaunchKernelGGL((reduce_kernel<BITS, LOG2B, SR, true>), dim3(1), dim3(kWave), 0, s, a,
+                       ntrips * U);
+  }
   return launch_status();
 }
 
