@@ -50,13 +50,14 @@ EF_BITS = 4
 METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HBM peak"
 
 # demangled kernel names as rocprofv3 reports them
-def kname_quant(bits, log2b, sr, dt, mode):
-    return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}>" \
-           f"(lowbit::QuantArgs)"
+def kname_quant(bits, log2b, sr, dt, mode, tail=False):
+    return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
+           f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
 
 
-def kname_reduce(bits, log2b, sr):
-    return f"void lowbit::reduce_kernel<{bits}, {log2b}, {str(sr).lower()}>(lowbit::ReduceArgs)"
+def kname_reduce(bits, log2b, sr, tail=False):
+    return f"void lowbit::reduce_kernel<{bits}, {log2b}, {str(sr).lower()}, " \
+           f"{str(tail).lower()}>(lowbit::ReduceArgs, long)"
 
 
 def kname_dequant(bits, apply, dt):
@@ -93,7 +94,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=int, default=32 << 20,
+    ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="elements of the bucket the CPU oracle processes (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -33,7 +33,7 @@ __device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* 
   const uint32_t piece = word >> off;
   if constexpr (BITS == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[j] = ((piece >> j) & 1u) ? s : -s;
+    for (int j = 0; j < 4; ++j) d[j] = signed_scale(piece, j, s);
   } else {
     const uint32_t tw = piece ^ G::FLIP;        // fields become two's-complement q
 #pragma unroll
@@ -97,9 +97,9 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
           const int64_t e0 = r0 + lo;
           uint16_t* out = static_cast<uint16_t*>(a.w_out) + r0 + lo;
           if (full) {
-            *reinterpret_cast<uint2*>(out) =
-                make_uint2(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16),
-                           f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16));
+            store_stream(reinterpret_cast<uint2*>(out),
+                         make_uint2(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16),
+                                    f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)));
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)

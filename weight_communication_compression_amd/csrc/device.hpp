@@ -152,6 +152,24 @@ __device__ __forceinline__ float group_max_nonneg(float x) {
   return __uint_as_float(v);
 }
 
+// 1-bit codes of N <= 32 values: bit j = 1 iff v[j] >= 0 (so -0 gives 1).
+// fl(v + 0) turns -0 into +0, so its sign bit is set exactly for v < 0;
+// v_alignbit shifts the word left by one and inserts that sign bit, two
+// instructions per value and no compare/select.  (A NaN codes by its sign.)
+template <int N>
+__device__ __forceinline__ uint32_t sign_codes(const float* v) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = N - 1; j >= 0; --j)
+    w = __builtin_amdgcn_alignbit(w, __float_as_uint(v[j] + 0.0f), 31);
+  return ~w & (N == 32 ? 0xFFFFFFFFu : ((1u << N) - 1u));
+}
+
+// The 1-bit dequantized value u ? s : -s for bit j of `word`, as a sign flip.
+__device__ __forceinline__ float signed_scale(uint32_t word, int j, float s) {
+  return __uint_as_float(__float_as_uint(s) ^ (((~word) << (31 - j)) & 0x80000000u));
+}
+
 // Adjacent-pairs tree sum of |v[0..N)| within one lane (N a power of two).
 template <int N>
 __device__ __forceinline__ float lane_abs_tree(const float* v) {
@@ -315,6 +333,23 @@ __device__ __forceinline__ void load_tail(const void* base, int64_t t0, uint32_t
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming stores: outputs are written once and read by a later kernel, so
+// they are stored non-temporally and do not linger as dirty cache lines whose
+// write-back the next kernel would pay for.
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) {
+  if (LOWBIT_NT_STORES) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
+  if (LOWBIT_NT_STORES) {
+    const u32x2 q = {v.x, v.y};
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(p));
+  } else {
+    *p = v;
+  }
+}
 
 template <int E>
 __device__ __forceinline__ void store_vec_f32(float* base, int64_t t0, uint32_t off, const float* v) {

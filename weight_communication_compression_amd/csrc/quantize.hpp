@@ -53,12 +53,7 @@ __device__ __forceinline__ void quantize_tile(
   uint32_t sign_word[R];
   if constexpr (BITS == 1) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < E; ++j) w |= (v[r][j] >= 0.0f ? 1u : 0u) << j;
-      sign_word[r] = w;
-    }
+    for (int r = 0; r < R; ++r) sign_word[r] = sign_codes<E>(v[r]);
   }
 
   // ---- block statistic and scale ----------------------------------------
@@ -100,7 +95,7 @@ __device__ __forceinline__ void quantize_tile(
       word = sign_word[r];
       if constexpr (WANT_DEQ) {
 #pragma unroll
-        for (int j = 0; j < E; ++j) deq[r][j] = ((word >> j) & 1u) ? sc.s : -sc.s;
+        for (int j = 0; j < E; ++j) deq[r][j] = signed_scale(word, j, sc.s);
       }
     } else {
       word = G::PACK_BIAS;
@@ -132,11 +127,11 @@ __device__ __forceinline__ void quantize_tile(
       }
     }
     if (full) {
-      cbase[wl] = word;
+      store_stream(cbase + wl, word);
     } else if (i0 < n) {
       const int64_t valid = n - i0;
       if (valid < E) word &= (1u << (valid * BITS)) - 1u;
-      cbase[wl] = word;
+      store_stream(cbase + wl, word);
     }
   }
 }

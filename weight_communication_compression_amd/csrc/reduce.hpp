@@ -39,7 +39,7 @@ __device__ __forceinline__ void accumulate_word(uint32_t word, float s, float* a
   if constexpr (BITS == 1) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const float d = ((word >> j) & 1u) ? s : -s;     // set: +s, clear: -s
+      const float d = signed_scale(word, j, s);          // set: +s, clear: -s
       acc[j] = FIRST ? d : acc[j] + d;
     }
   } else {
