@@ -57,12 +57,16 @@ struct Grid {
 #ifndef LOWBIT_SR_ELEMS_PER_TRIP
 #define LOWBIT_SR_ELEMS_PER_TRIP 16
 #endif
+#ifndef LOWBIT_BF16_ELEMS_PER_TRIP
+#define LOWBIT_BF16_ELEMS_PER_TRIP 8
+#endif
 
 // Tiles per loop trip for a kernel whose tile gives each lane PER_LANE
-// elements.
-template <int PER_LANE, bool SR = false>
+// elements (bfloat16 inputs may ask for more elements per trip: half the bytes).
+template <int PER_LANE, bool SR = false, bool HALF = false>
 constexpr int tiles_per_trip() {
-  constexpr int want = SR ? LOWBIT_SR_ELEMS_PER_TRIP : LOWBIT_ELEMS_PER_TRIP;
+  constexpr int base = SR ? LOWBIT_SR_ELEMS_PER_TRIP : LOWBIT_ELEMS_PER_TRIP;
+  constexpr int want = HALF && LOWBIT_BF16_ELEMS_PER_TRIP > base ? LOWBIT_BF16_ELEMS_PER_TRIP : base;
   return PER_LANE >= want ? 1 : want / PER_LANE;
 }
 

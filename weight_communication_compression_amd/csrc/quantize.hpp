@@ -197,7 +197,7 @@ template <int BITS, int LOG2B, bool SR, int DT, int MODE, bool TAIL>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
-  constexpr int U = tiles_per_trip<R * E, SR>();
+  constexpr int U = tiles_per_trip<R * E, SR, DT == kBF16>();
 
   if constexpr (TAIL) {
     if (global_wave_id() != 0) return;
