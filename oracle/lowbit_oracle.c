@@ -16,13 +16,18 @@
  *   - bitscom README, section "Backend Registration Options": the options
  *     bitwidth / block_size / error feedback, and the "legacy" error-feedback
  *     mode applied to the first-stage quantization.
+ *   - the same section: the "ef21" mode of the first-stage quantization and
+ *     the "ef21_plus" mode, which adds error feedback to the quantization of
+ *     the reduced shard.
  *   - SDP4Bit README, section "Overview": quantizing weight differences
  *     instead of weights; section "Weight Quantization Arguments": the bit
- *     count and group (block) size of weight quantization.
+ *     count and group (block) size of weight quantization; section "Gradient
+ *     Quantization Arguments": separate bit counts and group sizes for the
+ *     intra-node and the inter-node gradient quantization.
  *
  * The pages fix no formulas.  Each step below follows the plainest reading;
- * every reading is numbered (R1..R16) where it is used and listed in the
- * design notes of the repository.
+ * every reading is numbered (R1..R16, R23..R25) where it is used and listed
+ * in the design notes of the repository.
  *
  * Arithmetic: IEEE binary32 with round-to-nearest-even, one operation at a
  * time.  Build with  -O2 -ffp-contract=off -fno-fast-math  so that no
@@ -418,49 +423,114 @@ int oracle_ef_compress(const void* g, int32_t dtype, float* e, int64_t n, int32_
 }
 
 /*
+ * EF21 compress (bitscom README, "Backend Registration Options": the "ef21"
+ * error-feedback mode of the first-stage quantization; the page names the
+ * mode only, so the update follows the published EF21 method: each worker
+ * keeps a state h, sends the compressed difference between its gradient and
+ * h, and moves h by what it sent).  R23:
+ *   d_i = fl(g_i - h_i); quantize d; h_i <- fl(h_i + deq_i).
+ * The state h is binary32, owned by the caller, updated in place.
+ */
+int oracle_ef21_compress(const void* g, int32_t dtype, float* h, int64_t n, int32_t bits,
+                         int32_t block, int32_t stochastic, uint64_t seed, uint64_t index_offset,
+                         uint32_t* codes, uint16_t* scales)
+{
+    int rc = check_q(bits, block, n, index_offset);
+    if (rc) return rc;
+    int64_t nw = oracle_num_words(n, bits);
+    for (int64_t w = 0; w < nw; ++w) codes[w] = 0;
+    float* d = (float*)malloc(sizeof(float) * (size_t)block);
+    float* q = (float*)malloc(sizeof(float) * (size_t)block);
+    if (!d || !q) { free(d); free(q); return ORACLE_EINVAL; }
+    int64_t nb = oracle_num_blocks(n, block);
+    for (int64_t k = 0; k < nb; ++k) {
+        int64_t lo = k * block;
+        int64_t nvalid = (n - lo < block) ? (n - lo) : block;
+        for (int64_t j = 0; j < nvalid; ++j) d[j] = load_elem(g, dtype, lo + j) - h[lo + j];
+        scales[k] = quantize_block(d, nvalid, block, bits, bits == 1 ? 0 : stochastic,
+                                   seed, index_offset + (uint64_t)lo, codes, lo, q);
+        for (int64_t j = 0; j < nvalid; ++j) h[lo + j] = h[lo + j] + q[j];
+    }
+    free(d);
+    free(q);
+    return ORACLE_OK;
+}
+
+/*
  * Local reduce of the low-bit all-reduce (bitscom README, "Implemented
  * Features": all-to-all -> local reduce -> all-gather).  npeers chunks of the
- * same n elements, each packed with (in_bits, block) are dequantized and
+ * same n elements, each packed with (in_bits, in_block), are dequantized and
  * summed in binary32 in peer order (R15):
  *     acc = d_0;  acc = fl(acc + d_p) for p = 1 .. npeers-1
- * and the sum is quantized again with (out_bits, block, out_stochastic,
+ * where d_p of element i uses peer p's scale of input block i / in_block.
+ * The sum is quantized again with (out_bits, out_block, out_stochastic,
  * out_seed, out_index_offset).  out_sum, when not NULL, receives acc.
+ *
+ * Mixed widths and block sizes (SDP4Bit README, "Gradient Quantization
+ * Arguments": separate bit counts and group sizes for the intra-node and the
+ * inter-node gradient quantization, 8 and 4 bits by default) are the same
+ * computation with in_bits != out_bits or in_block != out_block (R24).
+ *
+ * Stage-2 error feedback (bitscom README, "Backend Registration Options":
+ * the "ef21_plus" mode also applies error feedback to the quantization of
+ * the reduced shard) when residual is not NULL, R25 (R14 on the sum):
+ *     a_i = fl(acc_i + e_i); quantize a; e_i <- fl(a_i - deq_i).
+ * out_sum still receives acc (before the residual is added).
  */
+int oracle_reduce_requant_ex(const uint32_t* const* peer_codes,
+                             const uint16_t* const* peer_scales, int32_t npeers, int64_t n,
+                             int32_t in_bits, int32_t in_block, int32_t out_bits,
+                             int32_t out_block, int32_t out_stochastic, uint64_t out_seed,
+                             uint64_t out_index_offset, float* residual, uint32_t* out_codes,
+                             uint16_t* out_scales, float* out_sum)
+{
+    if (npeers < 1 || npeers > 16) return ORACLE_EINVAL;
+    int rc = check_q(in_bits, in_block, n, 0);
+    if (rc) return rc;
+    rc = check_q(out_bits, out_block, n, out_index_offset);
+    if (rc) return rc;
+    int64_t nw = oracle_num_words(n, out_bits);
+    for (int64_t w = 0; w < nw; ++w) out_codes[w] = 0;
+    float* a = (float*)malloc(sizeof(float) * (size_t)out_block);
+    float* q = (float*)malloc(sizeof(float) * (size_t)out_block);
+    if (!a || !q) { free(a); free(q); return ORACLE_EINVAL; }
+    int64_t nb = oracle_num_blocks(n, out_block);
+    for (int64_t k = 0; k < nb; ++k) {
+        int64_t lo = k * out_block;
+        int64_t nvalid = (n - lo < out_block) ? (n - lo) : out_block;
+        for (int64_t j = 0; j < nvalid; ++j) {
+            int64_t i = lo + j;
+            float acc = 0.0f;
+            for (int32_t p = 0; p < npeers; ++p) {
+                float s = oracle_f16_to_f32(peer_scales[p][i / in_block]);
+                float d = dequant_code(get_code(peer_codes[p], i, in_bits), in_bits, s);
+                acc = (p == 0) ? d : acc + d;
+            }
+            if (out_sum) out_sum[i] = acc;
+            a[j] = residual ? acc + residual[i] : acc;
+        }
+        out_scales[k] = quantize_block(a, nvalid, out_block, out_bits,
+                                       out_bits == 1 ? 0 : out_stochastic, out_seed,
+                                       out_index_offset + (uint64_t)lo, out_codes, lo,
+                                       residual ? q : NULL);
+        if (residual)
+            for (int64_t j = 0; j < nvalid; ++j) residual[lo + j] = a[j] - q[j];
+    }
+    free(a);
+    free(q);
+    return ORACLE_OK;
+}
+
+/* The plain local reduce: one block size for input and output, no residual. */
 int oracle_reduce_requant(const uint32_t* const* peer_codes, const uint16_t* const* peer_scales,
                           int32_t npeers, int64_t n, int32_t in_bits, int32_t block,
                           int32_t out_bits, int32_t out_stochastic, uint64_t out_seed,
                           uint64_t out_index_offset, uint32_t* out_codes, uint16_t* out_scales,
                           float* out_sum)
 {
-    if (npeers < 1 || npeers > 16) return ORACLE_EINVAL;
-    if (!valid_bits(in_bits)) return ORACLE_EINVAL;
-    int rc = check_q(out_bits, block, n, out_index_offset);
-    if (rc) return rc;
-    int64_t nw = oracle_num_words(n, out_bits);
-    for (int64_t w = 0; w < nw; ++w) out_codes[w] = 0;
-    float* a = (float*)malloc(sizeof(float) * (size_t)block);
-    if (!a) return ORACLE_EINVAL;
-    int64_t nb = oracle_num_blocks(n, block);
-    for (int64_t k = 0; k < nb; ++k) {
-        int64_t lo = k * block;
-        int64_t nvalid = (n - lo < block) ? (n - lo) : block;
-        for (int64_t j = 0; j < nvalid; ++j) {
-            int64_t i = lo + j;
-            float acc = 0.0f;
-            for (int32_t p = 0; p < npeers; ++p) {
-                float s = oracle_f16_to_f32(peer_scales[p][k]);
-                float d = dequant_code(get_code(peer_codes[p], i, in_bits), in_bits, s);
-                acc = (p == 0) ? d : acc + d;
-            }
-            a[j] = acc;
-            if (out_sum) out_sum[i] = acc;
-        }
-        out_scales[k] = quantize_block(a, nvalid, block, out_bits,
-                                            out_bits == 1 ? 0 : out_stochastic, out_seed,
-                                            out_index_offset + (uint64_t)lo, out_codes, lo, NULL);
-    }
-    free(a);
-    return ORACLE_OK;
+    return oracle_reduce_requant_ex(peer_codes, peer_scales, npeers, n, in_bits, block, out_bits,
+                                    block, out_stochastic, out_seed, out_index_offset, NULL,
+                                    out_codes, out_scales, out_sum);
 }
 
 /*

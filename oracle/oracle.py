@@ -22,7 +22,8 @@ __all__ = [
     "f16_to_f32", "f32_to_f16_rne", "f16_round_up", "bf16_to_f32", "f32_to_bf16_rne",
     "fmix32", "sr_key", "sr_bits", "sr_uniform",
     "num_words", "num_blocks", "pack_codes", "unpack_codes",
-    "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
+    "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant", "reduce_requant_ex",
+    "ef21_compress",
     "wdiff_compress", "wdiff_apply",
     "F32", "BF16",
 ]
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
             "oracle_ef_compress": (ctypes.c_int, [P, i32, P, i64, i32, i32, i32, u64, u64, P, P]),
             "oracle_reduce_requant": (ctypes.c_int, [P, P, i32, i64, i32, i32, i32, i32, u64, u64,
                                                      P, P, P]),
+            "oracle_reduce_requant_ex": (ctypes.c_int, [P, P, i32, i64, i32, i32, i32, i32, i32,
+                                                        u64, u64, P, P, P, P]),
+            "oracle_ef21_compress": (ctypes.c_int, [P, i32, P, i64, i32, i32, i32, u64, u64, P, P]),
             "oracle_wdiff_compress": (ctypes.c_int, [P, P, i32, i64, i32, i32, i32, u64, u64, P, P]),
             "oracle_wdiff_apply": (ctypes.c_int, [P, P, P, i64, i32, i32, P, i32]),
             "oracle_f32_to_f16_rne_array": (None, [P, i64, P]),
@@ -253,6 +257,50 @@ def reduce_requant(peer_codes, peer_scales, n: int, in_bits: int, block: int, ou
                                        _ptr(codes), _ptr(scales),
                                        _ptr(total) if want_sum else None), "reduce_requant")
     return codes, scales, total
+
+
+def reduce_requant_ex(peer_codes, peer_scales, n: int, in_bits: int, in_block: int,
+                      out_bits: int, out_block: int, out_stochastic: bool = False,
+                      out_seed: int = 0, out_index_offset: int = 0, residual=None,
+                      want_sum: bool = False):
+    """General local reduce: separate input/output widths and block sizes and
+    an optional stage-2 residual.  Returns (codes, scales, sum_or_None,
+    new_residual_or_None); the input residual is not modified."""
+    P = len(peer_codes)
+    pc = [np.ascontiguousarray(c, dtype=np.uint32) for c in peer_codes]
+    ps = [np.ascontiguousarray(s, dtype=np.uint16) for s in peer_scales]
+    cp = (ctypes.c_void_p * max(P, 1))(*[_ptr(c) for c in pc])
+    sp = (ctypes.c_void_p * max(P, 1))(*[_ptr(s) for s in ps])
+    codes = np.empty(num_words(n, out_bits), np.uint32)
+    scales = np.empty(num_blocks(n, out_block), np.uint16)
+    total = np.empty(n, np.float32) if want_sum else None
+    e = None
+    if residual is not None:
+        e = np.array(residual, dtype=np.float32, copy=True)
+        assert e.size == n
+    _check(lib().oracle_reduce_requant_ex(ctypes.cast(cp, ctypes.c_void_p),
+                                          ctypes.cast(sp, ctypes.c_void_p), P, n, in_bits,
+                                          in_block, out_bits, out_block, int(out_stochastic),
+                                          out_seed, out_index_offset,
+                                          _ptr(e) if e is not None else None, _ptr(codes),
+                                          _ptr(scales), _ptr(total) if want_sum else None),
+           "reduce_requant_ex")
+    return codes, scales, total, e
+
+
+def ef21_compress(g, state, bits: int, block: int, stochastic: bool = False, seed: int = 0,
+                  index_offset: int = 0):
+    """Returns (codes, scales, new_state); the input state is not modified."""
+    dt, g = _as_input(g)
+    n = g.size
+    h = np.array(state, dtype=np.float32, copy=True)
+    assert h.size == n
+    codes = np.empty(num_words(n, bits), np.uint32)
+    scales = np.empty(num_blocks(n, block), np.uint16)
+    _check(lib().oracle_ef21_compress(_ptr(g), dt, _ptr(h), n, bits, block, int(stochastic),
+                                      seed, index_offset, _ptr(codes), _ptr(scales)),
+           "ef21_compress")
+    return codes, scales, h
 
 
 def wdiff_compress(w_new, w_old, bits: int, block: int, stochastic: bool = False, seed: int = 0,
