@@ -14,9 +14,15 @@
  *                (bitscom README, "Implemented Features" and "Backend
  *                Registration Options": the legacy mode on the first-stage
  *                quantization)
+ *   EF21 compress: compress (g - h), keep h <- h + deq(...) (bitscom README,
+ *                "Backend Registration Options": the "ef21" mode)
  *   local reduce + requantize: the middle stage of a low-bit all-reduce
  *                (all-to-all -> local reduce -> all-gather; bitscom README,
- *                "Implemented Features")
+ *                "Implemented Features"), optionally with error feedback on
+ *                the reduced shard (same page, "Backend Registration
+ *                Options": "ef21_plus") and with fewer output bits than input
+ *                bits (SDP4Bit README, "Gradient Quantization Arguments":
+ *                8-bit intra-node, 4-bit inter-node codes)
  *   weight-difference compress / apply (SDP4Bit README, "Overview" and
  *                "Weight Quantization Arguments")
  *
@@ -45,14 +51,15 @@
  *     arrays holding device pointers.  The caller allocates and owns every
  *     buffer, including the error-feedback residual; the library allocates
  *     nothing and keeps no state between calls.
- *   - Alignment: element buffers (x, g, residual, w_*, y) 16 bytes, codes
- *     4 bytes, scales 2 bytes.
+ *   - Alignment: element buffers (x, g, residual, state, w_*, y) 16 bytes,
+ *     codes 4 bytes (peer codes of a mixed-width reduce: 4 * b_in/b_out
+ *     bytes), scales 2 bytes.
  *   - Launches are asynchronous on `stream` (0 = the null stream).  Argument
  *     errors are reported synchronously and nothing is launched.  A launch
  *     failure returns LOWBIT_EDEVICE.  No call aborts or throws.
  *   - n == 0 is a no-op returning LOWBIT_OK.
- *   - Outputs must not alias inputs, except `residual` (in/out by design) and
- *     w_out == w_old in lowbit_wdiff_apply.
+ *   - Outputs must not alias inputs, except `residual` / `state` (in/out by
+ *     design) and w_out == w_old in lowbit_wdiff_apply.
  *   - Non-finite inputs give unspecified (but in-range) codes; calls still
  *     terminate normally.
  */
@@ -142,22 +149,57 @@ lowbit_status lowbit_ef_compress(const void* g, lowbit_dtype gt, float* residual
                                  hipStream_t stream);
 
 /*
+ * EF21 compress (bitscom README, "Backend Registration Options": the "ef21"
+ * mode of the first-stage quantization; the update is the published EF21
+ * one).  For every element
+ *     d = fl(g - h);  (codes, scales) = compress(d);  h <- fl(h + deq)
+ *   g     : device, n elements of type gt (read)
+ *   state : device, n binary32 (read and overwritten); the worker's EF21
+ *           state h, zero before the first step.  Receivers track the sum of
+ *           the states by adding the reduced messages (lowbit_wdiff_apply
+ *           with wt = LOWBIT_F32 computes that fl(h + deq)).
+ */
+lowbit_status lowbit_ef21_compress(const void* g, lowbit_dtype gt, float* state, int64_t n,
+                                   const lowbit_qparams* p, uint32_t* codes, uint16_t* scales,
+                                   hipStream_t stream);
+
+/*
  * Local reduce + requantize of a low-bit all-reduce (bitscom README,
  * "Implemented Features": all-to-all -> local reduce -> all-gather).  The
- * npeers chunks cover the same n elements; each is dequantized with in_p and
- * summed in binary32 in peer order,
+ * npeers chunks cover the same n elements; each is dequantized with in_p
+ * (its bitwidth and block size) and summed in binary32 in peer order,
  *     acc = d_0;  acc = fl(acc + d_p), p = 1 .. npeers-1,
- * and acc is compressed with out_p.
+ * and acc is compressed with out_p.  in_p and out_p may differ in block size
+ * and, for the pairs 8 -> 4, 8 -> 2 and 4 -> 2, in bitwidth (SDP4Bit README,
+ * "Gradient Quantization Arguments": 8-bit intra-node codes requantized to
+ * 4 bits for the inter-node step).  Only in_p's bitwidth and block_size are
+ * used.
  *   peer_codes, peer_scales : HOST arrays of npeers DEVICE pointers
  *   out_sum                 : device, n binary32 (written) or NULL to skip
- * EINVAL additionally: npeers outside [1, 16], in_p->block_size !=
- * out_p->block_size.  EUNSUPPORTED: in_p->bitwidth != out_p->bitwidth.
+ * EINVAL additionally: npeers outside [1, 16].  EUNSUPPORTED: any other pair
+ * of different bitwidths.
  */
 lowbit_status lowbit_reduce_requant(const uint32_t* const* peer_codes,
                                     const uint16_t* const* peer_scales, int32_t npeers, int64_t n,
                                     const lowbit_qparams* in_p, const lowbit_qparams* out_p,
                                     uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
                                     hipStream_t stream);
+
+/*
+ * Local reduce with stage-2 error feedback (bitscom README, "Backend
+ * Registration Options": "ef21_plus" adds error feedback to the quantization
+ * of the reduced shard).  As lowbit_reduce_requant, then per element
+ *     a = fl(acc + e);  (out_codes, out_scales) = compress(a);  e <- fl(a - deq)
+ *   residual : device, n binary32 (read and overwritten), zero before the
+ *              first step; must not be NULL.
+ *   out_sum  : receives acc (before e is added), or NULL.
+ */
+lowbit_status lowbit_reduce_requant_ef(const uint32_t* const* peer_codes,
+                                       const uint16_t* const* peer_scales, int32_t npeers,
+                                       int64_t n, const lowbit_qparams* in_p,
+                                       const lowbit_qparams* out_p, float* residual,
+                                       uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
+                                       hipStream_t stream);
 
 /*
  * Weight-difference compress (SDP4Bit README, "Overview": weights are sent

@@ -85,6 +85,11 @@ def test_entry_points_reject_bad_params(bad):
                                    None) == lb.EINVAL
     assert L.lowbit_reduce_requant(None, None, 2, 100, ctypes.byref(good), r, None, None, None,
                                    None) == lb.EINVAL
+    assert L.lowbit_ef21_compress(None, 0, None, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_reduce_requant_ef(None, None, 2, 100, r, ctypes.byref(good), None, None,
+                                      None, None, None) == lb.EINVAL
+    assert L.lowbit_reduce_requant_ef(None, None, 2, 100, ctypes.byref(good), r, None, None,
+                                      None, None, None) == lb.EINVAL
 
 
 def test_entry_points_reject_null_params_struct():
@@ -126,6 +131,9 @@ def test_zero_length_is_a_noop():
     assert L.lowbit_wdiff_compress(None, None, 1, 0, r, None, None, None) == lb.OK
     assert L.lowbit_wdiff_apply(None, None, None, 0, r, None, 1, None) == lb.OK
     assert L.lowbit_reduce_requant(None, None, 1, 0, r, r, None, None, None, None) == lb.OK
+    assert L.lowbit_reduce_requant_ef(None, None, 1, 0, r, r, None, None, None, None,
+                                      None) == lb.OK
+    assert L.lowbit_ef21_compress(None, 0, None, 0, r, None, None, None) == lb.OK
     assert L.lowbit_copy_f32(None, None, 0, None) == lb.OK
 
 
@@ -135,12 +143,36 @@ def test_reduce_argument_rules():
     for npeers in [0, -1, 17, 100]:
         assert L.lowbit_reduce_requant(None, None, npeers, 10, r, r, None, None, None,
                                        None) == lb.EINVAL
+        assert L.lowbit_reduce_requant_ef(None, None, npeers, 10, r, r, None, None, None,
+                                          None, None) == lb.EINVAL
+    # different block sizes are allowed: with NULL buffers the call reaches
+    # the pointer checks
     other_block = ctypes.byref(_qp(block_size=256))
     assert L.lowbit_reduce_requant(None, None, 2, 10, r, other_block, None, None, None,
                                    None) == lb.EINVAL
-    other_bits = ctypes.byref(_qp(bitwidth=8))
-    assert L.lowbit_reduce_requant(None, None, 2, 10, r, other_bits, None, None, None,
-                                   None) == lb.EUNSUPPORTED
+    # bitwidth pairs: 8->4, 8->2, 4->2 are supported, the others are not
+    for bi, bo in [(4, 8), (2, 4), (1, 2), (2, 1), (4, 1), (8, 1)]:
+        qi, qo = ctypes.byref(_qp(bitwidth=bi)), ctypes.byref(_qp(bitwidth=bo))
+        assert L.lowbit_reduce_requant(None, None, 2, 10, qi, qo, None, None, None,
+                                       None) == lb.EUNSUPPORTED
+        assert L.lowbit_reduce_requant_ef(None, None, 2, 10, qi, qo, None, None, None,
+                                          None, None) == lb.EUNSUPPORTED
+    for bi, bo in [(8, 4), (8, 2), (4, 2)]:
+        qi, qo = ctypes.byref(_qp(bitwidth=bi)), ctypes.byref(_qp(bitwidth=bo))
+        assert L.lowbit_reduce_requant(None, None, 2, 10, qi, qo, None, None, None,
+                                       None) == lb.EINVAL
+    # the stage-2 residual must be given
+    ok = ctypes.c_void_p(0x4000)
+    cp1 = (ctypes.c_void_p * 1)(ok)
+    assert L.lowbit_reduce_requant_ef(ctypes.cast(cp1, ctypes.c_void_p),
+                                      ctypes.cast(cp1, ctypes.c_void_p), 1, 10, r, r, None, ok,
+                                      ok, None, None) == lb.EINVAL
+    # mixed widths need peer codes aligned for the lane's vector load
+    q8, q4 = ctypes.byref(_qp(bitwidth=8)), ctypes.byref(_qp(bitwidth=4))
+    odd = (ctypes.c_void_p * 1)(ctypes.c_void_p(0x4004))
+    assert L.lowbit_reduce_requant(ctypes.cast(odd, ctypes.c_void_p),
+                                   ctypes.cast(cp1, ctypes.c_void_p), 1, 10, q8, q4, ok, ok,
+                                   None, None) == lb.EINVAL
     # a NULL entry in the peer pointer arrays is rejected before launch
     ok = ctypes.c_void_p(0x4000)
     cp = (ctypes.c_void_p * 2)(ok, None)

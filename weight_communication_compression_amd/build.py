@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblowbit.so")
 
 SOURCES = ["api.cpp", "quantize_plain.hip", "quantize_ef.hip", "quantize_wdiff.hip",
-           "reduce.hip", "dequant.hip"]
+           "quantize_ef21.hip", "reduce.hip", "reduce_ef.hip", "reduce_mixed.hip",
+           "dequant.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

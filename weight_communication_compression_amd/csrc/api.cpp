@@ -148,34 +148,90 @@ lowbit_status lowbit_ef_compress(const void* g, lowbit_dtype gt, float* residual
   return launch_quantize_ef(p->bitwidth, lb, p->stochastic != 0, (int)gt, a, stream);
 }
 
-lowbit_status lowbit_reduce_requant(const uint32_t* const* peer_codes,
-                                    const uint16_t* const* peer_scales, int32_t npeers, int64_t n,
-                                    const lowbit_qparams* in_p, const lowbit_qparams* out_p,
-                                    uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
-                                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two local-reduce entry points (residual == nullptr: no
+// stage-2 error feedback).
+lowbit_status reduce_common(const uint32_t* const* peer_codes, const uint16_t* const* peer_scales,
+                            int32_t npeers, int64_t n, const lowbit_qparams* in_p,
+                            const lowbit_qparams* out_p, float* residual, bool want_residual,
+                            uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
+                            hipStream_t stream) {
   const int lb_in = check_params(in_p);
   const int lb = check_params(out_p);
   if (lb_in < 0 || lb < 0 || n < 0 || n > kMaxN) return LOWBIT_EINVAL;
   if (npeers < 1 || npeers > kMaxPeers) return LOWBIT_EINVAL;
-  if (in_p->block_size != out_p->block_size) return LOWBIT_EINVAL;
-  if (in_p->bitwidth != out_p->bitwidth) return LOWBIT_EUNSUPPORTED;
+  const int bi = in_p->bitwidth, bo = out_p->bitwidth;
+  const bool mixed = bi != bo;
+  if (mixed && !((bi == 8 && (bo == 4 || bo == 2)) || (bi == 4 && bo == 2)))
+    return LOWBIT_EUNSUPPORTED;
   if (n == 0) return LOWBIT_OK;
   if (!peer_codes || !peer_scales || !out_codes || !out_scales) return LOWBIT_EINVAL;
+  if (want_residual && (!residual || !aligned(residual, 16))) return LOWBIT_EINVAL;
   if (!aligned(out_codes, 4) || !aligned(out_scales, 2) || (out_sum && !aligned(out_sum, 16)))
     return LOWBIT_EINVAL;
+  // a lane loads b_in/b_out input words as one vector
+  const uintptr_t in_align = mixed ? (uintptr_t)(4 * (bi / bo)) : 4;
   ReduceArgs a{};
   for (int p = 0; p < npeers; ++p) {
-    if (!peer_codes[p] || !peer_scales[p] || !aligned(peer_codes[p], 4) ||
+    if (!peer_codes[p] || !peer_scales[p] || !aligned(peer_codes[p], in_align) ||
         !aligned(peer_scales[p], 2))
       return LOWBIT_EINVAL;
     a.codes[p] = peer_codes[p];
     a.scales[p] = peer_scales[p];
   }
   a.npeers = npeers;
+  a.in_log2b = lb_in;
   a.n = n;
   a.out_sum = out_sum;
+  a.resid = residual;
   a.out = TileOut{out_codes, out_scales, out_p->index_offset, seed_key(out_p->seed)};
-  return launch_reduce(out_p->bitwidth, lb, out_p->stochastic != 0, a, stream);
+  const bool sr = out_p->stochastic != 0;
+  if (mixed) return launch_reduce_mixed(bi, bo, lb, sr, want_residual, a, stream);
+  return want_residual ? launch_reduce_same_ef(bo, lb, sr, a, stream)
+                       : launch_reduce_same(bo, lb, sr, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+lowbit_status lowbit_reduce_requant(const uint32_t* const* peer_codes,
+                                    const uint16_t* const* peer_scales, int32_t npeers, int64_t n,
+                                    const lowbit_qparams* in_p, const lowbit_qparams* out_p,
+                                    uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
+                                    hipStream_t stream) {
+  return reduce_common(peer_codes, peer_scales, npeers, n, in_p, out_p, nullptr, false, out_codes,
+                       out_scales, out_sum, stream);
+}
+
+lowbit_status lowbit_reduce_requant_ef(const uint32_t* const* peer_codes,
+                                       const uint16_t* const* peer_scales, int32_t npeers,
+                                       int64_t n, const lowbit_qparams* in_p,
+                                       const lowbit_qparams* out_p, float* residual,
+                                       uint32_t* out_codes, uint16_t* out_scales, float* out_sum,
+                                       hipStream_t stream) {
+  return reduce_common(peer_codes, peer_scales, npeers, n, in_p, out_p, residual, true, out_codes,
+                       out_scales, out_sum, stream);
+}
+
+lowbit_status lowbit_ef21_compress(const void* g, lowbit_dtype gt, float* state, int64_t n,
+                                   const lowbit_qparams* p, uint32_t* codes, uint16_t* scales,
+                                   hipStream_t stream) {
+  const int lb = check_params(p);
+  if (lb < 0 || n < 0 || n > kMaxN || !valid_dtype(gt)) return LOWBIT_EINVAL;
+  if (n == 0) return LOWBIT_OK;
+  if (!g || !state || !codes || !scales) return LOWBIT_EINVAL;
+  if (!aligned(g, 16) || !aligned(state, 16) || !aligned(codes, 4) || !aligned(scales, 2))
+    return LOWBIT_EINVAL;
+  QuantArgs a{};
+  a.x = g;
+  a.resid = state;
+  a.n = n;
+  a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
+  return launch_quantize_ef21(p->bitwidth, lb, p->stochastic != 0, (int)gt, a, stream);
 }
 
 lowbit_status lowbit_wdiff_compress(const void* w_new, const void* w_old, lowbit_dtype wt,

@@ -19,7 +19,7 @@ struct TileOut {
 struct QuantArgs {
   const void* x;          // plain: x;  error feedback: g;  weight diff: w_new
   const void* x2;         // weight diff: w_old
-  float* resid;           // error feedback: residual, read and overwritten
+  float* resid;           // error feedback: residual / EF21: state, read and overwritten
   int64_t n;
   TileOut out;
 };
@@ -28,8 +28,10 @@ struct ReduceArgs {
   const uint32_t* codes[kMaxPeers];
   const uint16_t* scales[kMaxPeers];
   int32_t npeers;
+  int32_t in_log2b;        // log2 of the peers' block size
   int64_t n;
   float* out_sum;          // may be null
+  float* resid;            // stage-2 error feedback: residual, read and overwritten
   TileOut out;
 };
 

@@ -136,10 +136,12 @@ __device__ __forceinline__ void quantize_tile(
   }
 }
 
-// Load one tile's values (x, plus the residual or minus the old weights).
+// Load one tile's values (x, plus the residual or minus the old weights or
+// minus the EF21 state).  EF21 keeps the state in `h` for finish_tile.
 template <int BITS, int LOG2B, int DT, int MODE, bool FULL>
 __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
-                                          float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
+                                          float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E],
+                                          float (&h)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
   const int lane = lane_id();
@@ -149,43 +151,54 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
     float w[E];
     if constexpr (FULL) {
       load_vec<DT, E>(a.x, t0, off, v[r]);
-      if constexpr (MODE == kErrorFeedback) load_vec<kF32, E>(a.resid, t0, off, w);
+      if constexpr (MODE == kErrorFeedback || MODE == kEF21) load_vec<kF32, E>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, t0, off, w);
     } else {
       load_tail<DT, E>(a.x, t0, off, a.n - t0, v[r]);
-      if constexpr (MODE == kErrorFeedback) load_tail<kF32, E>(a.resid, t0, off, a.n - t0, w);
+      if constexpr (MODE == kErrorFeedback || MODE == kEF21)
+        load_tail<kF32, E>(a.resid, t0, off, a.n - t0, w);
       if constexpr (MODE == kWeightDiff) load_tail<DT, E>(a.x2, t0, off, a.n - t0, w);
     }
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       if constexpr (MODE == kErrorFeedback) v[r][j] = v[r][j] + w[j];   // a = g + e
       if constexpr (MODE == kWeightDiff) v[r][j] = v[r][j] - w[j];      // w_new - w_old
+      if constexpr (MODE == kEF21) {
+        v[r][j] = v[r][j] - w[j];                                       // d = g - h
+        h[r][j] = w[j];
+      }
     }
   }
 }
 
-// Quantize one loaded tile; in error-feedback mode also write e = a - deq.
+// Quantize one loaded tile; in error-feedback mode also write e = a - deq,
+// in EF21 mode h + deq.
 template <int BITS, int LOG2B, bool SR, int MODE, bool FULL>
 __device__ __forceinline__ void finish_tile(const QuantArgs& a, int64_t t0,
-                                            const float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
+                                            const float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E],
+                                            const float (&h)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
-  constexpr bool EF = MODE == kErrorFeedback;
+  constexpr bool WANT_DEQ = MODE == kErrorFeedback || MODE == kEF21;
   const int lane = lane_id();
   float deq[R][E];
-  quantize_tile<BITS, LOG2B, SR, EF>(v, t0, a.n, FULL, a.out, deq);
-  if constexpr (EF) {
+  quantize_tile<BITS, LOG2B, SR, WANT_DEQ>(v, t0, a.n, FULL, a.out, deq);
+  if constexpr (WANT_DEQ) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t off = (uint32_t)(r * kWave + lane) * E;
       float e[E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) e[j] = v[r][j] - deq[r][j];          // e = a - deq
+      for (int j = 0; j < E; ++j) {
+        if constexpr (MODE == kErrorFeedback) e[j] = v[r][j] - deq[r][j];   // e = a - deq
+        else e[j] = h[r][j] + deq[r][j];                                    // h + deq
+      }
       if constexpr (FULL) store_vec_f32<E>(a.resid, t0, off, e);
       else store_tail_f32<E>(a.resid, t0, off, a.n - t0, e);
     }
   }
   (void)deq;
+  (void)h;
 }
 
 // Main kernel (TAIL = false): each wave takes one trip of U full tiles -- all
@@ -204,26 +217,26 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a, in
     const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
     for (int64_t tile = first; tile < ntiles; ++tile) {
       const int64_t t0 = tile * S::TILE;
-      float v[R][E];
+      float v[R][E], h[R][E];
       if (t0 + S::TILE <= a.n) {
-        load_tile<BITS, LOG2B, DT, MODE, true>(a, t0, v);
-        finish_tile<BITS, LOG2B, SR, MODE, true>(a, t0, v);
+        load_tile<BITS, LOG2B, DT, MODE, true>(a, t0, v, h);
+        finish_tile<BITS, LOG2B, SR, MODE, true>(a, t0, v, h);
       } else {
-        load_tile<BITS, LOG2B, DT, MODE, false>(a, t0, v);
-        finish_tile<BITS, LOG2B, SR, MODE, false>(a, t0, v);
+        load_tile<BITS, LOG2B, DT, MODE, false>(a, t0, v, h);
+        finish_tile<BITS, LOG2B, SR, MODE, false>(a, t0, v, h);
       }
     }
   } else {
     const int64_t ntrips = first / U;                 // first = number of full tiles
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
     for (int64_t trip = global_wave_id(); trip < ntrips; trip += nwaves) {
-      float v[U][R][E];
+      float v[U][R][E], h[U][R][E];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        load_tile<BITS, LOG2B, DT, MODE, true>(a, (trip * U + u) * S::TILE, v[u]);
+        load_tile<BITS, LOG2B, DT, MODE, true>(a, (trip * U + u) * S::TILE, v[u], h[u]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        finish_tile<BITS, LOG2B, SR, MODE, true>(a, (trip * U + u) * S::TILE, v[u]);
+        finish_tile<BITS, LOG2B, SR, MODE, true>(a, (trip * U + u) * S::TILE, v[u], h[u]);
     }
   }
 }

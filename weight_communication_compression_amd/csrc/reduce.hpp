@@ -1,12 +1,17 @@
 // reduce.hpp -- local reduce + requantize kernel: the middle stage of a
 // low-bit all-reduce.  Up to 16 peer chunks of the same element range are
 // decoded, summed in binary32 in peer order and compressed again, in one pass
-// over HBM.  Same tile layout as the compress kernel: lane l owns word
-// r*64 + l of the tile in every peer chunk and in the output.
+// over HBM.  Same tile layout as the compress kernel, on the output's
+// bitwidth and block size: lane l owns output word r*64 + l of the tile.
 //
-// The peer loop is not unrolled (the 32 peer pointers stay in the kernel
-// argument block and are fetched with scalar loads); the next peer's words
-// and scales are loaded while the current peer is decoded.
+// The peers may be packed with more bits than the output (8-bit intra-node
+// codes requantized to 4 bits for the inter-node exchange): an output word
+// of E = 32/b_out elements then covers M = b_in/b_out input words, which the
+// lane loads as one vector.  The input block size is a run-time value; a
+// lane's E elements always lie in one input block (E <= 32 <= input block).
+//
+// With a residual (stage-2 error feedback) the sum plus the residual is
+// quantized and the residual becomes what quantization left behind.
 #pragma once
 
 #include "quantize.hpp"
@@ -59,22 +64,56 @@ __device__ __forceinline__ void accumulate_word(uint32_t word, float s, float* a
   }
 }
 
-// Peer loop of one trip: W packed words per lane per peer.  Peers are taken
-// in groups of kPeerGroup; all loads of a group are issued before any of its
-// peers is decoded, so a whole group's reads are in flight together (the
-// group's peer pointers come from the kernel-argument block by scalar loads).
-// GUARD: some slots of the trip lie past the end of the buffer (read as 0).
-constexpr int kPeerGroup = 8;
+// Input words per output word, and their vector load.
+template <int IN_BITS, int BITS>
+constexpr int in_words() { return IN_BITS / BITS; }
 
-template <int BITS, int R, int W, bool GUARD>
+template <int M>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
+  if constexpr (M == 1) {
+    w[0] = *p;
+  } else if constexpr (M == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < M / 4; ++k) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k + 0] = t.x;
+      w[4 * k + 1] = t.y;
+      w[4 * k + 2] = t.z;
+      w[4 * k + 3] = t.w;
+    }
+  }
+}
+
+// Peer loop of one trip: W output words per lane, each fed by M input words
+// per peer.  Peers are taken in groups of G; all loads of a group are issued
+// before any of its peers is decoded, so a whole group's reads are in flight
+// together (the group's peer pointers come from the kernel-argument block by
+// scalar loads).  G is 8, fewer when a lane's share of a trip is large, so
+// that at most 32 loaded words per lane are held at once.  GUARD: some slots
+// of the trip lie past the end of the buffer (read as 0).
+template <int W, int M>
+constexpr int peer_group() {
+  return 32 / (W * M) >= 8 ? 8 : (32 / (W * M) >= 1 ? 32 / (W * M) : 1);
+}
+
+template <int IN_BITS, int BITS, int R, int W, bool GUARD>
 __device__ __forceinline__ void reduce_peers(const ReduceArgs& a, const int64_t* wt,
                                              const int64_t* kt, const uint32_t* wl,
                                              const uint32_t* kl, const bool* in,
                                              float (*acc)[Grid<BITS>::E]) {
+  constexpr int M = in_words<IN_BITS, BITS>();
+  constexpr int EIN = Grid<IN_BITS>::E;
+  constexpr int kPeerGroup = peer_group<W, M>();
   const int np = a.npeers;
+  const int64_t nwin = (a.n * IN_BITS + 31) / 32;       // input words per peer
+  (void)nwin;
 #pragma unroll 1
   for (int g = 0; g < np; g += kPeerGroup) {
-    uint32_t w[kPeerGroup][W], sc[kPeerGroup][W];
+    uint32_t w[kPeerGroup][W][M], sc[kPeerGroup][W];
 #pragma unroll
     for (int q = 0; q < kPeerGroup; ++q) {
       if (g + q < np) {                                   // wave-uniform
@@ -83,14 +122,13 @@ __device__ __forceinline__ void reduce_peers(const ReduceArgs& a, const int64_t*
 #pragma unroll
         for (int i = 0; i < W; ++i) {
           if (GUARD) {
-            w[q][i] = 0;
-            sc[q][i] = 0;
-            if (in[i]) {
-              w[q][i] = (cp + wt[i / R])[wl[i]];
-              sc[q][i] = (sp + kt[i / R])[kl[i]];
-            }
+            // word by word: the last output word's input words may end early
+            const int64_t w0 = wt[i / R] + (int64_t)wl[i] * M;
+#pragma unroll
+            for (int m = 0; m < M; ++m) w[q][i][m] = (in[i] && w0 + m < nwin) ? cp[w0 + m] : 0u;
+            sc[q][i] = in[i] ? (sp + kt[i / R])[kl[i]] : 0u;
           } else {
-            w[q][i] = (cp + wt[i / R])[wl[i]];
+            load_words<M>(cp + wt[i / R] + wl[i] * M, w[q][i]);
             sc[q][i] = (sp + kt[i / R])[kl[i]];
           }
         }
@@ -102,46 +140,74 @@ __device__ __forceinline__ void reduce_peers(const ReduceArgs& a, const int64_t*
 #pragma unroll
         for (int i = 0; i < W; ++i) {
           const float s = f16_bits_to_f32(sc[q][i]);
-          if (q == 0 && g == 0) accumulate_word<BITS, true>(w[q][i], s, acc[i]);
-          else accumulate_word<BITS, false>(w[q][i], s, acc[i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            if (q == 0 && g == 0) accumulate_word<IN_BITS, true>(w[q][i][m], s, acc[i] + m * EIN);
+            else accumulate_word<IN_BITS, false>(w[q][i][m], s, acc[i] + m * EIN);
+          }
         }
       }
     }
   }
 }
 
-// Reduce and requantize NT consecutive tiles starting at tile `tile0`.
+// Reduce and requantize NT consecutive output tiles starting at tile `tile0`.
 // GUARD: the tiles may reach past the end of the buffer (only in the tail
 // kernel): loads past the end read 0 and those positions are +0 for the
-// statistic.
-template <int BITS, int LOG2B, bool SR, int NT, bool GUARD>
+// statistic.  EF: stage-2 error feedback with the residual a.resid.
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD>
 __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R, W = NT * R;
+  constexpr int M = in_words<IN_BITS, BITS>();
+  constexpr int K = acc_shift<IN_BITS>();
+  constexpr float UNSCALE = 1.0f / (float)(1 << K);              // exact
+  // the statistic can absorb the 2^K of the sums unless it is the 1-bit mean
+  // or a residual is added first
+  constexpr bool UNSCALE_FIRST = EF || (BITS == 1 && K > 0);
   const int lane = lane_id();
   const int64_t n = a.n;
-  const int64_t nwords = (n + E - 1) / E;
+  const int64_t nwords = (n + E - 1) / E;           // output words
+  const int lbi = a.in_log2b;
 
-  // slot i = (tile u, row r): the tile's first word and block are
-  // wave-uniform; the lane's word and block within the tile are 32-bit
+  // slot i = (tile u, row r): the tile's first input word and input block
+  // are wave-uniform; the lane's output word and input block within the tile
+  // are 32-bit.  A tile either lies inside one input block or starts on a
+  // block boundary, so block(t0 + off) = block(t0) + (off >> lbi).
   int64_t wt[NT], kt[NT];
   uint32_t wl[W], kl[W];
   bool in[W];
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
-    wt[u] = (tile0 + u) * (S::TILE / E);
-    kt[u] = ((tile0 + u) * S::TILE) >> LOG2B;
+    const int64_t t0 = (tile0 + u) * S::TILE;
+    wt[u] = (t0 / E) * M;
+    kt[u] = t0 >> lbi;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t w = (uint32_t)(r * kWave + lane);
       wl[u * R + r] = w;
-      kl[u * R + r] = (w * E) >> LOG2B;
-      in[u * R + r] = !GUARD || wt[u] + w < nwords;
+      kl[u * R + r] = (w * E) >> lbi;
+      in[u * R + r] = !GUARD || t0 / E + w < nwords;
+    }
+  }
+
+  // stage-2 residual of the lane's elements, in flight with the first peers
+  float e[NT][R][E];
+  if constexpr (EF) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int64_t t0 = (tile0 + u) * S::TILE;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t off = (uint32_t)(r * kWave + lane) * E;
+        if (!GUARD || t0 + S::TILE <= n) load_vec<kF32, E>(a.resid, t0, off, e[u][r]);
+        else load_tail<kF32, E>(a.resid, t0, off, n - t0, e[u][r]);
+      }
     }
   }
 
   float acc[NT][R][E];
-  reduce_peers<BITS, R, W, GUARD>(a, wt, kt, wl, kl, in, &acc[0][0]);
+  reduce_peers<IN_BITS, BITS, R, W, GUARD>(a, wt, kt, wl, kl, in, &acc[0][0]);
 
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
@@ -152,10 +218,9 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < E; ++j)
-          if ((wt[u] + wl[u * R + r]) * E + j >= n) acc[u][r][j] = 0.0f;
+          if (t0 + (int64_t)wl[u * R + r] * E + j >= n) acc[u][r][j] = 0.0f;
     }
     if (a.out_sum) {
-      constexpr float UNSCALE = 1.0f / (float)(1 << acc_shift<BITS>());   // exact
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t off = (uint32_t)(r * kWave + lane) * E;
@@ -166,28 +231,53 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
         else store_tail_f32<E>(a.out_sum, t0, off, n - t0, sum);
       }
     }
-    float unused[R][E];
-    quantize_tile<BITS, LOG2B, SR, false, acc_shift<BITS>()>(acc[u], t0, n, full, a.out, unused);
-    (void)unused;
+    float deq[R][E];
+    if constexpr (UNSCALE_FIRST) {
+      // a = fl(sum + e): positions past the end stay +0 (e reads 0 there)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          acc[u][r][j] = acc[u][r][j] * UNSCALE;
+          if constexpr (EF) acc[u][r][j] = acc[u][r][j] + e[u][r][j];
+        }
+      quantize_tile<BITS, LOG2B, SR, EF, 0>(acc[u], t0, n, full, a.out, deq);
+    } else {
+      quantize_tile<BITS, LOG2B, SR, false, K>(acc[u], t0, n, full, a.out, deq);
+    }
+    if constexpr (EF) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t off = (uint32_t)(r * kWave + lane) * E;
+        float en[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) en[j] = acc[u][r][j] - deq[r][j];   // e = a - deq
+        if (full) store_vec_f32<E>(a.resid, t0, off, en);
+        else store_tail_f32<E>(a.resid, t0, off, n - t0, en);
+      }
+    }
+    (void)deq;
   }
+  (void)e;
 }
 
 // Main kernel (TAIL = false): each wave takes one trip of U full tiles; the
 // grid covers the complete trips of full tiles only (`first` = number of full
 // tiles).  Tail kernel (TAIL = true, one wave): tiles from `first` on.
-template <int BITS, int LOG2B, bool SR, bool TAIL>
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL>
 __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
   if constexpr (TAIL) {
     if (global_wave_id() != 0) return;
     const int64_t ntiles = (a.n + S::TILE - 1) / S::TILE;
-    for (int64_t tile = first; tile < ntiles; ++tile) reduce_tiles<BITS, LOG2B, SR, 1, true>(a, tile);
+    for (int64_t tile = first; tile < ntiles; ++tile)
+      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, 1, true>(a, tile);
   } else {
     const int64_t ntrips = first / U;
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
     for (int64_t trip = global_wave_id(); trip < ntrips; trip += nwaves)
-      reduce_tiles<BITS, LOG2B, SR, U, false>(a, trip * U);
+      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false>(a, trip * U);
   }
 }
 

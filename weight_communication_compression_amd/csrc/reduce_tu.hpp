@@ -1,0 +1,44 @@
+// reduce_tu.hpp -- launch helpers for the local-reduce kernels; each
+// translation unit instantiates one family (same width, same width with a
+// residual, mixed widths).
+#pragma once
+
+#include "launch.hpp"
+#include "reduce.hpp"
+
+namespace lowbit {
+
+// Main kernel over the complete trips of full tiles; one-wave tail kernel for
+// whatever remains.
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF>
+static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
+  const int64_t full_tiles = a.n / S::TILE;
+  const int64_t ntrips = full_tiles / U;
+  if (ntrips > 0) {
+    hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, false>),
+                       dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+  }
+  if (ntrips * U * S::TILE < a.n) {
+    hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, true>), dim3(1), dim3(kWave),
+                       0, s, a, ntrips * U);
+  }
+  return launch_status();
+}
+
+// stochastic rounding does not apply to a 1-bit output
+template <int IN_BITS, int BITS, bool EF>
+static lowbit_status launch_r_b(int log2b, bool sr, const ReduceArgs& a, hipStream_t s) {
+  switch (log2b) {
+#define LOWBIT_CASE(LB)                                                       \
+  case LB:                                                                    \
+    return (BITS > 1 && sr) ? launch_r<IN_BITS, BITS, LB, (BITS > 1), EF>(a, s) \
+                            : launch_r<IN_BITS, BITS, LB, false, EF>(a, s);
+    LOWBIT_FOR_EACH_LOG2B(LOWBIT_CASE)
+#undef LOWBIT_CASE
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+}  // namespace lowbit

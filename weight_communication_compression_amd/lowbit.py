@@ -66,7 +66,9 @@ def lib() -> ctypes.CDLL:
             "lowbit_quantize_pack": (ctypes.c_int, [P, ctypes.c_int, i64, QP, P, P, P]),
             "lowbit_unpack_dequant": (ctypes.c_int, [P, P, i64, QP, P, P]),
             "lowbit_ef_compress": (ctypes.c_int, [P, ctypes.c_int, P, i64, QP, P, P, P]),
+            "lowbit_ef21_compress": (ctypes.c_int, [P, ctypes.c_int, P, i64, QP, P, P, P]),
             "lowbit_reduce_requant": (ctypes.c_int, [P, P, i32, i64, QP, QP, P, P, P, P]),
+            "lowbit_reduce_requant_ef": (ctypes.c_int, [P, P, i32, i64, QP, QP, P, P, P, P, P]),
             "lowbit_wdiff_compress": (ctypes.c_int, [P, P, ctypes.c_int, i64, QP, P, P, P]),
             "lowbit_wdiff_apply": (ctypes.c_int, [P, P, P, i64, QP, P, ctypes.c_int, P]),
             "lowbit_copy_f32": (ctypes.c_int, [P, P, i64, P]),
@@ -196,24 +198,37 @@ def ef_compress(g: torch.Tensor, residual: torch.Tensor, bitwidth: int, block_si
     return codes, scales
 
 
-def reduce_requant(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[torch.Tensor],
-                   n: int, bitwidth: int, block_size: int, stochastic: bool = False,
-                   seed: int = 0, index_offset: int = 0, out_codes=None, out_scales=None,
-                   out_sum=None, want_sum: bool = False):
-    """Local reduce: dequantize npeers chunks, sum in peer order, requantize.
+def ef21_compress(g: torch.Tensor, state: torch.Tensor, bitwidth: int, block_size: int,
+                  stochastic: bool = False, seed: int = 0, index_offset: int = 0,
+                  codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """EF21 compress of g - state; `state` (float32[n]) becomes state + deq, in place."""
+    n = g.numel()
+    if state.dtype != torch.float32 or state.numel() != n:
+        raise LowbitError(EINVAL, "state must be float32 with g.numel() elements")
+    codes = _out_codes(n, bitwidth, g, codes)
+    scales = _out_scales(n, block_size, g, scales)
+    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset)
+    _check(lib().lowbit_ef21_compress(_dev(g, "g"), _dtype_code(g), _dev(state, "state"), n,
+                                      ctypes.byref(qp), _dev(codes, "codes"),
+                                      _dev(scales, "scales"), _stream(g)), "lowbit_ef21_compress")
+    return codes, scales
 
-    Returns (codes, scales, sum_or_None)."""
+
+def _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed, index_offset,
+            out_codes, out_scales, out_sum, want_sum, out_bitwidth, out_block_size, residual):
     P = len(peer_codes)
     if P != len(peer_scales):
         raise LowbitError(EINVAL, "peer_codes and peer_scales differ in length")
     if P < 1:
         raise LowbitError(EINVAL, "reduce_requant needs at least one peer")
+    ob = bitwidth if out_bitwidth is None else out_bitwidth
+    oB = block_size if out_block_size is None else out_block_size
     for c, sc in zip(peer_codes, peer_scales):
         _need_codes(c, n, bitwidth, "peer codes")
         _need_scales(sc, n, block_size, "peer scales")
     like = peer_codes[0]
-    out_codes = _out_codes(n, bitwidth, like, out_codes)
-    out_scales = _out_scales(n, block_size, like, out_scales)
+    out_codes = _out_codes(n, ob, like, out_codes)
+    out_scales = _out_scales(n, oB, like, out_scales)
     if want_sum and out_sum is None:
         out_sum = torch.empty(n, dtype=torch.float32, device=like.device)
     if out_sum is not None and (out_sum.dtype != torch.float32 or out_sum.numel() < n):
@@ -221,14 +236,53 @@ def reduce_requant(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[tor
     cp = (ctypes.c_void_p * P)(*[_dev(c, "peer codes") for c in peer_codes])
     sp = (ctypes.c_void_p * P)(*[_dev(s, "peer scales") for s in peer_scales])
     qi = _qp(bitwidth, block_size)
-    qo = _qp(bitwidth, block_size, stochastic, seed, index_offset)
-    _check(lib().lowbit_reduce_requant(ctypes.cast(cp, ctypes.c_void_p),
-                                       ctypes.cast(sp, ctypes.c_void_p), P, n, ctypes.byref(qi),
-                                       ctypes.byref(qo), _dev(out_codes, "out_codes"),
-                                       _dev(out_scales, "out_scales"),
-                                       _dev(out_sum, "out_sum") if out_sum is not None else None,
-                                       _stream(like)), "lowbit_reduce_requant")
+    qo = _qp(ob, oB, stochastic, seed, index_offset)
+    tail = (_dev(out_codes, "out_codes"), _dev(out_scales, "out_scales"),
+            _dev(out_sum, "out_sum") if out_sum is not None else None, _stream(like))
+    if residual is None:
+        _check(lib().lowbit_reduce_requant(ctypes.cast(cp, ctypes.c_void_p),
+                                           ctypes.cast(sp, ctypes.c_void_p), P, n,
+                                           ctypes.byref(qi), ctypes.byref(qo), *tail),
+               "lowbit_reduce_requant")
+    else:
+        if residual.dtype != torch.float32 or residual.numel() != n:
+            raise LowbitError(EINVAL, "residual must be float32 with n elements")
+        _check(lib().lowbit_reduce_requant_ef(ctypes.cast(cp, ctypes.c_void_p),
+                                              ctypes.cast(sp, ctypes.c_void_p), P, n,
+                                              ctypes.byref(qi), ctypes.byref(qo),
+                                              _dev(residual, "residual"), *tail),
+               "lowbit_reduce_requant_ef")
     return out_codes, out_scales, out_sum
+
+
+def reduce_requant(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[torch.Tensor],
+                   n: int, bitwidth: int, block_size: int, stochastic: bool = False,
+                   seed: int = 0, index_offset: int = 0, out_codes=None, out_scales=None,
+                   out_sum=None, want_sum: bool = False, out_bitwidth: Optional[int] = None,
+                   out_block_size: Optional[int] = None):
+    """Local reduce: dequantize npeers chunks packed with (bitwidth,
+    block_size), sum in peer order, requantize with (out_bitwidth,
+    out_block_size) (default: the same) and the rounding options.
+
+    Returns (codes, scales, sum_or_None)."""
+    return _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed,
+                   index_offset, out_codes, out_scales, out_sum, want_sum, out_bitwidth,
+                   out_block_size, None)
+
+
+def reduce_requant_ef(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[torch.Tensor],
+                      n: int, bitwidth: int, block_size: int, residual: torch.Tensor,
+                      stochastic: bool = False, seed: int = 0, index_offset: int = 0,
+                      out_codes=None, out_scales=None, out_sum=None, want_sum: bool = False,
+                      out_bitwidth: Optional[int] = None, out_block_size: Optional[int] = None):
+    """Local reduce with stage-2 error feedback: the sum plus `residual`
+    (float32[n], updated in place) is requantized.  Returns (codes, scales,
+    sum_or_None); the sum is taken before the residual is added."""
+    if residual is None:
+        raise LowbitError(EINVAL, "reduce_requant_ef needs a residual")
+    return _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed,
+                   index_offset, out_codes, out_scales, out_sum, want_sum, out_bitwidth,
+                   out_block_size, residual)
 
 
 def wdiff_compress(w_new: torch.Tensor, w_old: torch.Tensor, bitwidth: int, block_size: int,
