@@ -23,10 +23,11 @@
  *     instead of weights; section "Weight Quantization Arguments": the bit
  *     count and group (block) size of weight quantization; section "Gradient
  *     Quantization Arguments": separate bit counts and group sizes for the
- *     intra-node and the inter-node gradient quantization.
+ *     intra-node and the inter-node gradient quantization, and the Hadamard
+ *     transform applied before gradient quantization.
  *
  * The pages fix no formulas.  Each step below follows the plainest reading;
- * every reading is numbered (R1..R16, R23..R25) where it is used and listed
+ * every reading is numbered (R1..R16, R23..R26) where it is used and listed
  * in the design notes of the repository.
  *
  * Arithmetic: IEEE binary32 with round-to-nearest-even, one operation at a
@@ -386,6 +387,91 @@ int oracle_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t
     for (int64_t i = 0; i < n; ++i) {
         float s = oracle_f16_to_f32(scales[i / block]);
         y[i] = dequant_code(get_code(codes, i, bits), bits, s);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Hadamard smoothing (SDP4Bit README, "Gradient Quantization Arguments": a
+ * Hadamard transform of the gradient before quantization lowers the
+ * quantization error; "Overview": the two-level gradient smooth
+ * quantization).  R26: each block of B elements is transformed by the
+ * Sylvester-ordered Walsh-Hadamard matrix (H_1 = [1], H_2m = [[H_m, H_m],
+ * [H_m, -H_m]]), computed in binary32 by butterflies of stride 1, 2, ..., B/2
+ * in that order, each butterfly (a, b) -> (fl(a + b), fl(a - b)).  The
+ * forward result is multiplied by 2^-floor(L/2) and the inverse by
+ * 2^-ceil(L/2), L = log2 B, so the pair is the identity in exact arithmetic
+ * and both scalings are exact.  n must be a multiple of B.
+ */
+static void walsh_hadamard(float* t, int64_t B)
+{
+    for (int64_t h = 1; h < B; h <<= 1)
+        for (int64_t i = 0; i < B; i += 2 * h)
+            for (int64_t j = i; j < i + h; ++j) {
+                float a = t[j], b = t[j + h];
+                t[j] = a + b;
+                t[j + h] = a - b;
+            }
+}
+
+static int log2_of(int64_t B)
+{
+    int L = 0;
+    while (((int64_t)1 << L) < B) ++L;
+    return L;
+}
+
+int oracle_hadamard_quantize_pack(const void* x, int32_t dtype, int64_t n, int32_t bits,
+                                  int32_t block, int32_t stochastic, uint64_t seed,
+                                  uint64_t index_offset, uint32_t* codes, uint16_t* scales)
+{
+    int rc = check_q(bits, block, n, index_offset);
+    if (rc) return rc;
+    if (n % block != 0) return ORACLE_EINVAL;
+    int64_t nw = oracle_num_words(n, bits);
+    for (int64_t w = 0; w < nw; ++w) codes[w] = 0;
+    float* a = (float*)malloc(sizeof(float) * (size_t)block);
+    if (!a) return ORACLE_EINVAL;
+    float f = ldexpf(1.0f, -(log2_of(block) / 2));
+    int64_t nb = n / block;
+    for (int64_t k = 0; k < nb; ++k) {
+        int64_t lo = k * block;
+        for (int64_t j = 0; j < block; ++j) a[j] = load_elem(x, dtype, lo + j);
+        walsh_hadamard(a, block);
+        for (int64_t j = 0; j < block; ++j) a[j] = a[j] * f;
+        scales[k] = quantize_block(a, block, block, bits, bits == 1 ? 0 : stochastic, seed,
+                                   index_offset + (uint64_t)lo, codes, lo, NULL);
+    }
+    free(a);
+    return ORACLE_OK;
+}
+
+int oracle_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t n,
+                                   int32_t bits, int32_t block, float* y)
+{
+    if (!valid_bits(bits) || !valid_block(block) || n < 0) return ORACLE_EINVAL;
+    if (n % block != 0) return ORACLE_EINVAL;
+    float f = ldexpf(1.0f, -((log2_of(block) + 1) / 2));
+    for (int64_t lo = 0; lo < n; lo += block) {
+        float s = oracle_f16_to_f32(scales[lo / block]);
+        for (int64_t j = 0; j < block; ++j)
+            y[lo + j] = dequant_code(get_code(codes, lo + j, bits), bits, s);
+        walsh_hadamard(y + lo, block);
+        for (int64_t j = 0; j < block; ++j) y[lo + j] = y[lo + j] * f;
+    }
+    return ORACLE_OK;
+}
+
+/* The transform alone (forward: inverse = 0, inverse: inverse = 1), on whole
+ * blocks of x in place. */
+int oracle_hadamard_blocks(float* x, int64_t n, int32_t block, int32_t inverse)
+{
+    if (!valid_block(block) || n < 0 || n % block != 0) return ORACLE_EINVAL;
+    int L = log2_of(block);
+    float f = ldexpf(1.0f, inverse ? -((L + 1) / 2) : -(L / 2));
+    for (int64_t lo = 0; lo < n; lo += block) {
+        walsh_hadamard(x + lo, block);
+        for (int64_t j = 0; j < block; ++j) x[lo + j] = x[lo + j] * f;
     }
     return ORACLE_OK;
 }

@@ -23,7 +23,7 @@ __all__ = [
     "fmix32", "sr_key", "sr_bits", "sr_uniform",
     "num_words", "num_blocks", "pack_codes", "unpack_codes",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant", "reduce_requant_ex",
-    "ef21_compress",
+    "ef21_compress", "hadamard_quantize_pack", "hadamard_unpack_dequant", "hadamard_blocks",
     "wdiff_compress", "wdiff_apply",
     "F32", "BF16",
 ]
@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
             "oracle_reduce_requant_ex": (ctypes.c_int, [P, P, i32, i64, i32, i32, i32, i32, i32,
                                                         u64, u64, P, P, P, P]),
             "oracle_ef21_compress": (ctypes.c_int, [P, i32, P, i64, i32, i32, i32, u64, u64, P, P]),
+            "oracle_hadamard_quantize_pack": (ctypes.c_int, [P, i32, i64, i32, i32, i32, u64, u64,
+                                                             P, P]),
+            "oracle_hadamard_unpack_dequant": (ctypes.c_int, [P, P, i64, i32, i32, P]),
+            "oracle_hadamard_blocks": (ctypes.c_int, [P, i64, i32, i32]),
             "oracle_wdiff_compress": (ctypes.c_int, [P, P, i32, i64, i32, i32, i32, u64, u64, P, P]),
             "oracle_wdiff_apply": (ctypes.c_int, [P, P, P, i64, i32, i32, P, i32]),
             "oracle_f32_to_f16_rne_array": (None, [P, i64, P]),
@@ -301,6 +305,36 @@ def ef21_compress(g, state, bits: int, block: int, stochastic: bool = False, see
                                       seed, index_offset, _ptr(codes), _ptr(scales)),
            "ef21_compress")
     return codes, scales, h
+
+
+def hadamard_quantize_pack(x, bits: int, block: int, stochastic: bool = False, seed: int = 0,
+                           index_offset: int = 0):
+    """Blockwise Hadamard transform, then compress.  Returns (codes, scales)."""
+    dt, x = _as_input(x)
+    n = x.size
+    codes = np.empty(num_words(n, bits), np.uint32)
+    scales = np.empty(num_blocks(n, block), np.uint16)
+    _check(lib().oracle_hadamard_quantize_pack(_ptr(x), dt, n, bits, block, int(stochastic),
+                                               seed, index_offset, _ptr(codes), _ptr(scales)),
+           "hadamard_quantize_pack")
+    return codes, scales
+
+
+def hadamard_unpack_dequant(codes, scales, n: int, bits: int, block: int) -> np.ndarray:
+    """Decompress, then the inverse blockwise Hadamard transform."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    y = np.empty(n, np.float32)
+    _check(lib().oracle_hadamard_unpack_dequant(_ptr(codes), _ptr(scales), n, bits, block,
+                                                _ptr(y)), "hadamard_unpack_dequant")
+    return y
+
+
+def hadamard_blocks(x, block: int, inverse: bool = False) -> np.ndarray:
+    """The scaled blockwise transform alone (a copy of x is transformed)."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    _check(lib().oracle_hadamard_blocks(_ptr(y), y.size, block, int(inverse)), "hadamard_blocks")
+    return y
 
 
 def wdiff_compress(w_new, w_old, bits: int, block: int, stochastic: bool = False, seed: int = 0,
