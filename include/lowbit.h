@@ -14,6 +14,9 @@
  *                (bitscom README, "Implemented Features" and "Backend
  *                Registration Options": the legacy mode on the first-stage
  *                quantization)
+ *   Hadamard smoothing: blockwise Walsh-Hadamard transform before compress
+ *                and after decompress (SDP4Bit README, "Gradient Quantization
+ *                Arguments")
  *   EF21 compress: compress (g - h), keep h <- h + deq(...) (bitscom README,
  *                "Backend Registration Options": the "ef21" mode)
  *   local reduce + requantize: the middle stage of a low-bit all-reduce
@@ -134,6 +137,32 @@ lowbit_status lowbit_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
  */
 lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t n,
                                     const lowbit_qparams* p, float* y, hipStream_t stream);
+
+/*
+ * Compress with Hadamard smoothing (SDP4Bit README, "Gradient Quantization
+ * Arguments": a Hadamard transform before gradient quantization lowers the
+ * quantization error).  Each block of B elements is first transformed by the
+ * Sylvester-ordered Walsh-Hadamard matrix -- butterflies (a, b) -> (fl(a+b),
+ * fl(a-b)) of stride 1, 2, ..., B/2 in that order on binary32 values -- and
+ * multiplied by 2^-floor(L/2), L = log2 B; the result is compressed as by
+ * lowbit_quantize_pack (same wire format, same rounding options).  The local
+ * reduce is linear and works on such codes unchanged.
+ *   n must be a multiple of block_size (EINVAL otherwise); block_size above
+ *   2048 returns EUNSUPPORTED.
+ */
+lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
+                                            const lowbit_qparams* p, uint32_t* codes,
+                                            uint16_t* scales, hipStream_t stream);
+
+/*
+ * Decompress with the inverse smoothing: dequantize, apply the same
+ * butterflies per block and multiply by 2^-ceil(L/2) (the two scalings
+ * multiply to 1/B, so the pair of transforms is the identity in exact
+ * arithmetic).  Same size rules as lowbit_hadamard_quantize_pack.
+ */
+lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales,
+                                             int64_t n, const lowbit_qparams* p, float* y,
+                                             hipStream_t stream);
 
 /*
  * Error-feedback compress, legacy mode (bitscom README, "Implemented

@@ -86,6 +86,8 @@ def test_entry_points_reject_bad_params(bad):
     assert L.lowbit_reduce_requant(None, None, 2, 100, ctypes.byref(good), r, None, None, None,
                                    None) == lb.EINVAL
     assert L.lowbit_ef21_compress(None, 0, None, 100, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 128, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_hadamard_unpack_dequant(None, None, 128, r, None, None) == lb.EINVAL
     assert L.lowbit_reduce_requant_ef(None, None, 2, 100, r, ctypes.byref(good), None, None,
                                       None, None, None) == lb.EINVAL
     assert L.lowbit_reduce_requant_ef(None, None, 2, 100, ctypes.byref(good), r, None, None,
@@ -134,6 +136,23 @@ def test_zero_length_is_a_noop():
     assert L.lowbit_reduce_requant_ef(None, None, 1, 0, r, r, None, None, None, None,
                                       None) == lb.OK
     assert L.lowbit_ef21_compress(None, 0, None, 0, r, None, None, None) == lb.OK
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 0, r, None, None, None) == lb.OK
+    assert L.lowbit_hadamard_unpack_dequant(None, None, 0, r, None, None) == lb.OK
+
+
+def test_hadamard_size_rules():
+    L = lb.lib()
+    r = ctypes.byref(_qp(block_size=128))
+    # partial blocks are rejected; blocks above 2048 are not supported
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 200, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_hadamard_unpack_dequant(None, None, 200, r, None, None) == lb.EINVAL
+    big = ctypes.byref(_qp(block_size=4096))
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 8192, big, None, None,
+                                           None) == lb.EUNSUPPORTED
+    assert L.lowbit_hadamard_unpack_dequant(None, None, 8192, big, None,
+                                            None) == lb.EUNSUPPORTED
+    # whole blocks of a supported size reach the pointer checks
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 256, r, None, None, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, 0, None) == lb.OK
 
 

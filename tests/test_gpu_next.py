@@ -6,7 +6,10 @@ through the C ABI, against the CPU oracle on the same seeded inputs:
 * local reduce with stage-2 error feedback, chained over rounds;
 * local reduce with fewer output bits than input bits (8 -> 4, 8 -> 2,
   4 -> 2) and different input/output block sizes, with and without the
-  residual.
+  residual;
+* compress and decompress with blockwise Hadamard smoothing (the GPU
+  decompress is fed the GPU codes and checked against the oracle's
+  decompress of the same codes).
 
 Codes, scales, sums, residuals and states are compared bit for bit, at sizes
 that span several tiles and a ragged tail (including a last output word whose
@@ -167,3 +170,37 @@ def test_reduce_unsupported_pairs_raise():
     for bo in (8, 1):
         with pytest.raises(L.LowbitError):
             L.reduce_requant(gc, gs, n, 4, 128, out_bitwidth=bo)
+
+
+# ------------------------------------------------- Hadamard smoothing ----
+HS_BLOCKS = [32, 64, 128, 256, 512, 1024, 2048]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("B", HS_BLOCKS)
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_hadamard_compress_decompress(bits, B, sr, dtype):
+    T = _tile(bits, B)
+    for i, n in enumerate(sorted({B, 3 * B, 4 * T + B, 9 * T})):
+        x = mixed_input(3000 + bits * B + i, n) if i % 2 else \
+            np.random.default_rng(i).standard_t(3, n).astype(np.float32)
+        xin = bf16_bits_of(x) if dtype == "bf16" else x
+        say(f"hadamard compress bits={bits} B={B} sr={sr} {dtype} n={n}")
+        c, s = L.hadamard_quantize_pack(to_gpu(xin), bits, B, sr, 13, B * 2)
+        torch.cuda.synchronize()
+        wc, ws = O.hadamard_quantize_pack(xin, bits, B, sr, 13, B * 2)
+        assert_same(scales_np(s), ws, f"scales n={n}")
+        assert_same(codes_np(c), wc, f"codes n={n}")
+        say(f"hadamard decompress bits={bits} B={B} n={n}")
+        y = L.hadamard_unpack_dequant(c, s, n, bits, B)
+        torch.cuda.synchronize()
+        assert_same(f32_np(y), O.hadamard_unpack_dequant(wc, ws, n, bits, B), f"values n={n}")
+
+
+def test_hadamard_size_rules_raise():
+    x = torch.zeros(200, device="cuda")
+    with pytest.raises(L.LowbitError):
+        L.hadamard_quantize_pack(x, 4, 128)
+    with pytest.raises(L.LowbitError):
+        L.hadamard_quantize_pack(torch.zeros(8192, device="cuda"), 4, 4096)

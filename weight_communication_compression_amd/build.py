@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblowbit.so")
 
 SOURCES = ["api.cpp", "quantize_plain.hip", "quantize_ef.hip", "quantize_wdiff.hip",
-           "quantize_ef21.hip", "reduce.hip", "reduce_ef.hip", "reduce_mixed.hip",
+           "quantize_ef21.hip", "quantize_hadamard.hip", "reduce.hip", "reduce_ef.hip", "reduce_mixed.hip",
            "dequant.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -131,6 +131,44 @@ lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scale
   return launch_dequant(p->bitwidth, false, LOWBIT_F32, a, stream);
 }
 
+// Hadamard smoothing: whole blocks only; blocks up to 2048 elements (the
+// decompress transform runs within one 2048-element trip).
+lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
+                                            const lowbit_qparams* p, uint32_t* codes,
+                                            uint16_t* scales, hipStream_t stream) {
+  const int lb = check_params(p);
+  if (lb < 0 || n < 0 || n > kMaxN || !valid_dtype(xt)) return LOWBIT_EINVAL;
+  if (n % p->block_size != 0) return LOWBIT_EINVAL;
+  if (p->block_size > 2048) return LOWBIT_EUNSUPPORTED;
+  if (n == 0) return LOWBIT_OK;
+  if (!x || !codes || !scales) return LOWBIT_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;
+  QuantArgs a{};
+  a.x = x;
+  a.n = n;
+  a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
+  return launch_quantize_hadamard(p->bitwidth, lb, p->stochastic != 0, (int)xt, a, stream);
+}
+
+lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales,
+                                             int64_t n, const lowbit_qparams* p, float* y,
+                                             hipStream_t stream) {
+  const int lb = check_params(p);
+  if (lb < 0 || n < 0 || n > kMaxN) return LOWBIT_EINVAL;
+  if (n % p->block_size != 0) return LOWBIT_EINVAL;
+  if (p->block_size > 2048) return LOWBIT_EUNSUPPORTED;
+  if (n == 0) return LOWBIT_OK;
+  if (!codes || !scales || !y) return LOWBIT_EINVAL;
+  if (!aligned(y, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;
+  DequantArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.n = n;
+  a.log2b = lb;
+  a.y = y;
+  return launch_hadamard_dequant(p->bitwidth, a, stream);
+}
+
 lowbit_status lowbit_ef_compress(const void* g, lowbit_dtype gt, float* residual, int64_t n,
                                  const lowbit_qparams* p, uint32_t* codes, uint16_t* scales,
                                  hipStream_t stream) {

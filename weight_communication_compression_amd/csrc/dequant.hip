@@ -30,6 +30,39 @@ lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a,
   return LOWBIT_EUNSUPPORTED;
 }
 
+template <int BITS, int LOG2B>
+static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
+  const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
+  const int64_t ntrips = (nrows + kHadamardRows - 1) / kHadamardRows;
+  hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>), dim3(grid_for_tiles(ntrips)),
+                     dim3(kBlockThreads), 0, s, a);
+  return launch_status();
+}
+
+template <int BITS>
+static lowbit_status launch_hd_b(const DequantArgs& a, hipStream_t s) {
+  switch (a.log2b) {
+    case 5: return launch_hd<BITS, 5>(a, s);
+    case 6: return launch_hd<BITS, 6>(a, s);
+    case 7: return launch_hd<BITS, 7>(a, s);
+    case 8: return launch_hd<BITS, 8>(a, s);
+    case 9: return launch_hd<BITS, 9>(a, s);
+    case 10: return launch_hd<BITS, 10>(a, s);
+    case 11: return launch_hd<BITS, 11>(a, s);
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
+lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_hd_b<1>(a, s);
+    case 2: return launch_hd_b<2>(a, s);
+    case 4: return launch_hd_b<4>(a, s);
+    case 8: return launch_hd_b<8>(a, s);
+  }
+  return LOWBIT_EUNSUPPORTED;
+}
+
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
   const int64_t nvec = n / 4;
   int64_t blocks = (nvec + kCopyUnroll * kBlockThreads - 1) / (kCopyUnroll * kBlockThreads);

@@ -11,6 +11,7 @@
 
 #include "args.hpp"
 #include "device.hpp"
+#include "hadamard.hpp"
 
 namespace lowbit {
 
@@ -107,6 +108,55 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
           }
         }
       }
+    }
+  }
+}
+
+// Decompress followed by the inverse blockwise Walsh-Hadamard transform
+// (blocks of B = 2^LOG2B <= 2048 elements; n is a multiple of B).  Same
+// element-centric layout; a trip of 8 rows (2048 elements) holds whole
+// blocks, so the transform runs in registers: elements within the lane,
+// then lanes, then rows.  Loads and stores are guarded, the transform is
+// not (every lane of the wave takes part in the exchanges; lanes past the
+// end hold zeros of blocks that are not stored).
+constexpr int kHadamardRows = 8;
+
+template <int BITS, int LOG2B>
+__global__ __launch_bounds__(kBlockThreads) void hadamard_dequant_kernel(DequantArgs a) {
+  constexpr int E = Grid<BITS>::E;
+  constexpr int B = 1 << LOG2B;
+  static_assert(B <= kHadamardRows * kDeqRow, "a block must fit in one trip");
+  constexpr int LANES = B >= kDeqRow ? kWave : B / 4;
+  constexpr int ROWS_PER_BLOCK = B >= kDeqRow ? B / kDeqRow : 1;
+  const int lane = lane_id();
+  const int64_t wave = global_wave_id();
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n = a.n;
+  const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
+  const uint32_t lo = 4u * (uint32_t)lane;
+
+  for (int64_t base = wave * kHadamardRows; base < nrows; base += nwaves * kHadamardRows) {
+    uint32_t word[kHadamardRows], s16[kHadamardRows];
+#pragma unroll
+    for (int r = 0; r < kHadamardRows; ++r) {
+      const int64_t r0 = (base + r) * kDeqRow;
+      word[r] = 0;
+      s16[r] = 0;
+      if (r0 + lo < n) {
+        word[r] = (a.codes + r0 / E)[lo / E];
+        s16[r] = LOG2B >= 8 ? a.scales[r0 >> LOG2B] : (a.scales + (r0 >> LOG2B))[lo >> LOG2B];
+      }
+    }
+    float d[kHadamardRows][4];
+#pragma unroll
+    for (int r = 0; r < kHadamardRows; ++r)
+      decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
+    hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK>(d, hadamard_inverse_scale<LOG2B>());
+#pragma unroll
+    for (int r = 0; r < kHadamardRows; ++r) {
+      const int64_t r0 = (base + r) * kDeqRow;
+      // n is a multiple of B >= 32, so a lane's 4 elements are all valid or none
+      if (r0 + lo < n) store_vec_f32<4>(a.y, r0, lo, d[r]);
     }
   }
 }

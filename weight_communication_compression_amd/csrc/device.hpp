@@ -24,8 +24,9 @@ constexpr float kMagic = 12582912.0f;           // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;    // bit pattern of kMagic
 
 // compress modes: plain; error feedback (a = g + e, e <- a - deq); weight
-// difference (w_new - w_old); EF21 (d = g - h, h <- h + deq)
-enum Mode : int { kPlain = 0, kErrorFeedback = 1, kWeightDiff = 2, kEF21 = 3 };
+// difference (w_new - w_old); EF21 (d = g - h, h <- h + deq); Hadamard
+// smoothing (blockwise Walsh-Hadamard transform, then plain compress)
+enum Mode : int { kPlain = 0, kErrorFeedback = 1, kWeightDiff = 2, kEF21 = 3, kHadamard = 4 };
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
 template <int BITS>

@@ -41,7 +41,7 @@ inline lowbit_status launch_status() {
   return hipGetLastError() == hipSuccess ? LOWBIT_OK : LOWBIT_EDEVICE;
 }
 
-// mode: 0 plain, 1 error feedback, 2 weight difference, 3 EF21
+// mode: 0 plain, 1 error feedback, 2 weight difference, 3 EF21, 4 Hadamard
 lowbit_status launch_quantize_plain(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
                                     hipStream_t s);
 lowbit_status launch_quantize_ef(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
@@ -50,6 +50,8 @@ lowbit_status launch_quantize_wdiff(int bits, int log2b, bool sr, int dt, const 
                                     hipStream_t s);
 lowbit_status launch_quantize_ef21(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
                                    hipStream_t s);
+lowbit_status launch_quantize_hadamard(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
+                                       hipStream_t s);
 // local reduce: same width in and out, without / with a stage-2 residual;
 // mixed widths (in_bits > bits) for the pairs 8->4, 8->2, 4->2
 lowbit_status launch_reduce_same(int bits, int log2b, bool sr, const ReduceArgs& a,
@@ -59,6 +61,8 @@ lowbit_status launch_reduce_same_ef(int bits, int log2b, bool sr, const ReduceAr
 lowbit_status launch_reduce_mixed(int in_bits, int bits, int log2b, bool sr, bool ef,
                                   const ReduceArgs& a, hipStream_t s);
 lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a, hipStream_t s);
+// decompress + inverse Hadamard, blocks of 32 .. 2048
+lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_t s);
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
 
 }  // namespace lowbit

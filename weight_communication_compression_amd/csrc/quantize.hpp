@@ -17,6 +17,7 @@
 
 #include "args.hpp"
 #include "device.hpp"
+#include "hadamard.hpp"
 
 namespace lowbit {
 
@@ -169,6 +170,9 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
       }
     }
   }
+  // the tile holds whole blocks: B / E lanes of one row, or all R rows
+  if constexpr (MODE == kHadamard)
+    hadamard_rows<R, E, S::L, R>(v, hadamard_forward_scale<LOG2B>());
 }
 
 // Quantize one loaded tile; in error-feedback mode also write e = a - deq,

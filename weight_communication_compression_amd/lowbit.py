@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "lowbit_unpack_dequant": (ctypes.c_int, [P, P, i64, QP, P, P]),
             "lowbit_ef_compress": (ctypes.c_int, [P, ctypes.c_int, P, i64, QP, P, P, P]),
             "lowbit_ef21_compress": (ctypes.c_int, [P, ctypes.c_int, P, i64, QP, P, P, P]),
+            "lowbit_hadamard_quantize_pack": (ctypes.c_int, [P, ctypes.c_int, i64, QP, P, P, P]),
+            "lowbit_hadamard_unpack_dequant": (ctypes.c_int, [P, P, i64, QP, P, P]),
             "lowbit_reduce_requant": (ctypes.c_int, [P, P, i32, i64, QP, QP, P, P, P, P]),
             "lowbit_reduce_requant_ef": (ctypes.c_int, [P, P, i32, i64, QP, QP, P, P, P, P, P]),
             "lowbit_wdiff_compress": (ctypes.c_int, [P, P, ctypes.c_int, i64, QP, P, P, P]),
@@ -179,6 +181,38 @@ def unpack_dequant(codes: torch.Tensor, scales: torch.Tensor, n: int, bitwidth: 
     _check(lib().lowbit_unpack_dequant(_dev(codes, "codes"), _dev(scales, "scales"), n,
                                        ctypes.byref(qp), _dev(out, "out"), _stream(codes)),
            "lowbit_unpack_dequant")
+    return out
+
+
+def hadamard_quantize_pack(x: torch.Tensor, bitwidth: int, block_size: int,
+                           stochastic: bool = False, seed: int = 0, index_offset: int = 0,
+                           codes: Optional[torch.Tensor] = None,
+                           scales: Optional[torch.Tensor] = None):
+    """Blockwise Walsh-Hadamard transform of x, then compress; x.numel() must
+    be a multiple of block_size (<= 2048)."""
+    n = x.numel()
+    codes = _out_codes(n, bitwidth, x, codes)
+    scales = _out_scales(n, block_size, x, scales)
+    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset)
+    _check(lib().lowbit_hadamard_quantize_pack(_dev(x, "x"), _dtype_code(x), n, ctypes.byref(qp),
+                                               _dev(codes, "codes"), _dev(scales, "scales"),
+                                               _stream(x)), "lowbit_hadamard_quantize_pack")
+    return codes, scales
+
+
+def hadamard_unpack_dequant(codes: torch.Tensor, scales: torch.Tensor, n: int, bitwidth: int,
+                            block_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decompress, then the inverse blockwise transform -> float32[n]."""
+    _need_codes(codes, n, bitwidth, "codes")
+    _need_scales(scales, n, block_size, "scales")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    if out.dtype != torch.float32 or out.numel() < n:
+        raise LowbitError(EINVAL, "out must be float32 with >= n elements")
+    qp = _qp(bitwidth, block_size)
+    _check(lib().lowbit_hadamard_unpack_dequant(_dev(codes, "codes"), _dev(scales, "scales"), n,
+                                                ctypes.byref(qp), _dev(out, "out"),
+                                                _stream(codes)), "lowbit_hadamard_unpack_dequant")
     return out
 
 
