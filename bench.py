@@ -25,6 +25,12 @@ timed with HIP events on the stream the kernels run on; `traffic` comes from
 the committed rocprofv3 counter summary when it was taken on the current
 kernel sources.  `cpu_baseline` times the CPU oracle on a bounded sample of
 the same workload.
+
+`next_rows` (not part of `value`) times the extension kernels alone on
+their own workloads: EF21 compress and Hadamard-smoothed compress /
+decompress of the bucket, and the local reduce of 8 peer chunks of 32 Mi with
+stage-2 error feedback (b4 B128) and with two-level requantization (8-bit
+B512 peers to 4-bit B128).
 """
 from __future__ import annotations
 
@@ -94,6 +100,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--next-rows", type=int, default=1,
+                    help="also time the extension kernels alone (1) or not (0)")
     ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="elements of the bucket the CPU oracle processes (0 = skip)")
     args = ap.parse_args()
@@ -260,6 +268,9 @@ def main() -> int:
                       "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
                for i, s in enumerate(stages)}
 
+    # ----------------------------------------- extensions beyond the step --
+    next_rows = measure_next_rows(L, lib, dev, stream, x) if args.next_rows else None
+
     # ------------------------------------------------------- CPU oracle --
     cpu = None
     if args.cpu_sample > 0:
@@ -282,8 +293,107 @@ def main() -> int:
         "cpu_baseline": cpu,
         "kernels": kernels,
     }
+    if next_rows is not None:
+        out["next_rows"] = next_rows
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measure_next_rows(L, lib, dev, stream, x, reps=20):
+    """Kernels of the extensions beyond the step (not part of `value`): each
+    timed alone with HIP events on `stream`, median of `reps` launches, every
+    launch after a 1 GiB read that leaves the Infinity Cache clean.
+    Returns {name: {"workload", "us", "alg_bytes", "alg_GBps", "frac"}}."""
+    import torch
+    from weight_communication_compression_amd import synth
+
+    P = ctypes.c_void_p
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    N = x.numel()
+    out = {}
+
+    def qp(bits, block, sr=False, seed=0, off=0):
+        return L.QParams(bits, block, int(sr), 0, seed, off)
+
+    def timed(name, workload, alg_bytes, fn, args):
+        for _ in range(3):
+            st = fn(*args)
+            if st != 0:
+                raise L.LowbitError(st, fn.__name__)
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
+                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3)}
+
+    # EF21 compress of the bucket (b4 B256 SR), state carried in place
+    state = torch.zeros(N, dtype=torch.float32, device=dev)
+    nw, nb = L.num_words(N, 4), L.num_blocks(N, BLOCK)
+    c = torch.empty(nw, dtype=torch.int32, device=dev)
+    s = torch.empty(nb, dtype=torch.float16, device=dev)
+    q = qp(4, BLOCK, True, SEED)
+    timed("ef21_compress b4", f"{N} fp32 bucket, b4 B{BLOCK} SR", 3 * N * 4 + nw * 4 + nb * 2,
+          lib.lowbit_ef21_compress,
+          (P(x.data_ptr()), L.F32, P(state.data_ptr()), N, ctypes.byref(q), P(c.data_ptr()),
+           P(s.data_ptr()), sh))
+    del state
+
+    # Hadamard-smoothed compress / decompress of the bucket (b4 B128 SR)
+    HB = 128
+    nw, nb = L.num_words(N, 4), L.num_blocks(N, HB)
+    c = torch.empty(nw, dtype=torch.int32, device=dev)
+    s = torch.empty(nb, dtype=torch.float16, device=dev)
+    yh = torch.empty(N, dtype=torch.float32, device=dev)
+    qh = qp(4, HB, True, SEED)
+    hb = N * 4 + nw * 4 + nb * 2
+    timed("hadamard_quantize_pack b4", f"{N} fp32 bucket, b4 B{HB} SR", hb,
+          lib.lowbit_hadamard_quantize_pack,
+          (P(x.data_ptr()), L.F32, N, ctypes.byref(qh), P(c.data_ptr()), P(s.data_ptr()), sh))
+    timed("hadamard_unpack_dequant b4", f"{N} elements, b4 B{HB}", hb,
+          lib.lowbit_hadamard_unpack_dequant,
+          (P(c.data_ptr()), P(s.data_ptr()), N, ctypes.byref(qh), P(yh.data_ptr()), sh))
+    del yh, c, s
+
+    # 8 peer chunks of 32 Mi (the local-reduce configuration): stage-2 EF at
+    # b4 B128, and the two-level 8-bit B512 -> 4-bit B128 requantization
+    NP = synth.PEER_N
+    pc8, ps8, pc4, ps4 = [], [], [], []
+    for p in range(PEERS):
+        xp = torch.from_numpy(synth.peer_input(p)).to(dev)
+        a8, b8 = L.quantize_pack(xp, 8, 512)
+        a4, b4 = L.quantize_pack(xp, 4, 128)
+        pc8.append(a8), ps8.append(b8), pc4.append(a4), ps4.append(b4)
+        del xp
+    oc = torch.empty(L.num_words(NP, 4), dtype=torch.int32, device=dev)
+    os_ = torch.empty(L.num_blocks(NP, 128), dtype=torch.float16, device=dev)
+    out_bytes = oc.numel() * 4 + os_.numel() * 2
+    resid = torch.zeros(NP, dtype=torch.float32, device=dev)
+    cp = (P * PEERS)(*[t.data_ptr() for t in pc4])
+    sp = (P * PEERS)(*[t.data_ptr() for t in ps4])
+    qi, qo = qp(4, 128), qp(4, 128)
+    timed("reduce_requant_ef b4", f"{PEERS} x {NP} peers, b4 B128 -> b4 B128 + fp32 residual",
+          (PEERS + 1) * out_bytes + 2 * NP * 4, lib.lowbit_reduce_requant_ef,
+          (ctypes.cast(cp, P), ctypes.cast(sp, P), PEERS, NP, ctypes.byref(qi), ctypes.byref(qo),
+           P(resid.data_ptr()), P(oc.data_ptr()), P(os_.data_ptr()), None, sh))
+    cp8 = (P * PEERS)(*[t.data_ptr() for t in pc8])
+    sp8 = (P * PEERS)(*[t.data_ptr() for t in ps8])
+    qi8 = qp(8, 512)
+    in8 = L.num_words(NP, 8) * 4 + L.num_blocks(NP, 512) * 2
+    timed("reduce_requant b8->b4", f"{PEERS} x {NP} peers, b8 B512 -> b4 B128",
+          PEERS * in8 + out_bytes, lib.lowbit_reduce_requant,
+          (ctypes.cast(cp8, P), ctypes.cast(sp8, P), PEERS, NP, ctypes.byref(qi8),
+           ctypes.byref(qo), P(oc.data_ptr()), P(os_.data_ptr()), None, sh))
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(x, w_prev, w_new, n, nstages):
