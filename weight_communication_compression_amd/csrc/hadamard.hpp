@@ -7,8 +7,8 @@
 // stride picks which bit of the element's index within the block pairs the
 // two operands; with the data spread over the wave, low index bits are the
 // element within the lane, then the lane, then the row.  A cross-lane stage
-// reads the partner lane's value (DPP for lanes 1 and 2 apart, ds_swizzle up
-// to 16, ds_bpermute for 32) and each lane computes fma(own, +-1, partner):
+// reads the partner lane's value (ds_swizzle up to 16 lanes apart,
+// ds_bpermute for 32) and each lane computes fma(own, +-1, partner):
 // the product is exact, so this is fl(own + partner) in the lower lane and
 // fl(partner - own) in the upper one.  All lanes of the wave must be active.
 #pragma once
@@ -17,14 +17,19 @@
 
 namespace lowbit {
 
-// v[lane ^ D], D = 1 .. 32
+// Exchange unit for partners 1 and 2 lanes apart: ds_swizzle (the LDS pipe,
+// leaving the vector ALU to the butterflies) or DPP (a vector-ALU move).
+#ifndef LOWBIT_HS_DPP
+#define LOWBIT_HS_DPP 0
+#endif
+
+// v[lane ^ D], D = 1 .. 32: ds_swizzle in bit-mask mode (and 0x1F, xor D)
+// within each half-wave, ds_bpermute across the halves
 template <int D>
 __device__ __forceinline__ float xor_lane(float v) {
-  if constexpr (D == 1) return dpp_f32<0xB1>(v);               // quad_perm [1,0,3,2]
-  else if constexpr (D == 2) return dpp_f32<0x4E>(v);          // quad_perm [2,3,0,1]
-  else if constexpr (D == 4) return swizzle_f32<0x101F>(v);    // xor 4 within 32
-  else if constexpr (D == 8) return swizzle_f32<0x201F>(v);    // xor 8 within 32
-  else if constexpr (D == 16) return swizzle_f32<0x401F>(v);   // xor 16 within 32
+  if constexpr (D == 1 && LOWBIT_HS_DPP) return dpp_f32<0xB1>(v);       // quad_perm [1,0,3,2]
+  else if constexpr (D == 2 && LOWBIT_HS_DPP) return dpp_f32<0x4E>(v);  // quad_perm [2,3,0,1]
+  else if constexpr (D <= 16) return swizzle_f32<0x1F | (D << 10)>(v);
   else return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, __float_as_int(v)));
 }
 

@@ -21,6 +21,24 @@
 
 namespace lowbit {
 
+// Hadamard-smoothed compress spends more vector-ALU work per element; it may
+// take more tiles per trip to keep more loads in flight per wave.
+#ifndef LOWBIT_HS_ELEMS_PER_TRIP
+#define LOWBIT_HS_ELEMS_PER_TRIP 32
+#endif
+
+// Tiles per trip of the compress kernel for a tile of PER_LANE elements per
+// lane, by rounding, input type and mode.
+template <int PER_LANE, bool SR, int DT, int MODE>
+constexpr int compress_tiles_per_trip() {
+  if constexpr (MODE == kHadamard) {
+    constexpr int want = LOWBIT_HS_ELEMS_PER_TRIP;
+    return PER_LANE >= want ? 1 : want / PER_LANE;
+  } else {
+    return tiles_per_trip<PER_LANE, SR, DT == kBF16>();
+  }
+}
+
 template <int BITS, int LOG2B>
 struct TileShape {
   static constexpr int E = Grid<BITS>::E;
@@ -214,7 +232,7 @@ template <int BITS, int LOG2B, bool SR, int DT, int MODE, bool TAIL>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(QuantArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
-  constexpr int U = tiles_per_trip<R * E, SR, DT == kBF16>();
+  constexpr int U = compress_tiles_per_trip<R * E, SR, DT, MODE>();
 
   if constexpr (TAIL) {
     if (global_wave_id() != 0) return;

@@ -13,7 +13,7 @@ namespace lowbit {
 template <int BITS, int LOG2B, bool SR, int DT, int MODE>
 static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
   using S = TileShape<BITS, LOG2B>;
-  constexpr int U = tiles_per_trip<S::R * S::E, SR, DT == kBF16>();
+  constexpr int U = compress_tiles_per_trip<S::R * S::E, SR, DT, MODE>();
   const int64_t full_tiles = a.n / S::TILE;
   const int64_t ntrips = full_tiles / U;
   if (ntrips > 0) {
