@@ -61,9 +61,13 @@ def kname_quant(bits, log2b, sr, dt, mode, tail=False):
            f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
 
 
-def kname_reduce(bits, log2b, sr, tail=False):
-    return f"void lowbit::reduce_kernel<{bits}, {log2b}, {str(sr).lower()}, " \
-           f"{str(tail).lower()}>(lowbit::ReduceArgs, long)"
+def kname_reduce(in_bits, bits, log2b, sr, ef=False, tail=False):
+    return f"void lowbit::reduce_kernel<{in_bits}, {bits}, {log2b}, {str(sr).lower()}, " \
+           f"{str(ef).lower()}, {str(tail).lower()}>(lowbit::ReduceArgs, long)"
+
+
+def kname_hadamard_dequant(bits, log2b):
+    return f"void lowbit::hadamard_dequant_kernel<{bits}, {log2b}>(lowbit::DequantArgs)"
 
 
 def kname_dequant(bits, apply, dt):
@@ -161,7 +165,7 @@ def main() -> int:
         keep += [cp, spp, rc, rs, qi, qo]
         a = (ctypes.cast(cp, P), ctypes.cast(spp, P), PEERS, share, ctypes.byref(qi),
              ctypes.byref(qo), P(rc.data_ptr()), P(rs.data_ptr()), None, sh)
-        stages.append((f"reduce_requant b{b}", kname_reduce(b, 8, False),
+        stages.append((f"reduce_requant b{b}", kname_reduce(b, b, 8, False),
                        (PEERS + 1) * (snw * 4 + snb * 2), (lib.lowbit_reduce_requant, a)))
 
         qd = qp(b, BLOCK)
@@ -316,7 +320,7 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
     def qp(bits, block, sr=False, seed=0, off=0):
         return L.QParams(bits, block, int(sr), 0, seed, off)
 
-    def timed(name, workload, alg_bytes, fn, args):
+    def timed(name, workload, alg_bytes, fn, args, kernel):
         for _ in range(3):
             st = fn(*args)
             if st != 0:
@@ -333,7 +337,8 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
         ms = sorted(ts)[len(ts) // 2]
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
-                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3)}
+                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3),
+                     "kernel": kernel, "traffic": read_traffic(kernel)}
 
     # EF21 compress of the bucket (b4 B256 SR), state carried in place
     state = torch.zeros(N, dtype=torch.float32, device=dev)
@@ -344,7 +349,7 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
     timed("ef21_compress b4", f"{N} fp32 bucket, b4 B{BLOCK} SR", 3 * N * 4 + nw * 4 + nb * 2,
           lib.lowbit_ef21_compress,
           (P(x.data_ptr()), L.F32, P(state.data_ptr()), N, ctypes.byref(q), P(c.data_ptr()),
-           P(s.data_ptr()), sh))
+           P(s.data_ptr()), sh), kname_quant(4, 8, True, 0, 3))
     del state
 
     # Hadamard-smoothed compress / decompress of the bucket (b4 B128 SR)
@@ -357,10 +362,12 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
     hb = N * 4 + nw * 4 + nb * 2
     timed("hadamard_quantize_pack b4", f"{N} fp32 bucket, b4 B{HB} SR", hb,
           lib.lowbit_hadamard_quantize_pack,
-          (P(x.data_ptr()), L.F32, N, ctypes.byref(qh), P(c.data_ptr()), P(s.data_ptr()), sh))
+          (P(x.data_ptr()), L.F32, N, ctypes.byref(qh), P(c.data_ptr()), P(s.data_ptr()), sh),
+          kname_quant(4, 7, True, 0, 4))
     timed("hadamard_unpack_dequant b4", f"{N} elements, b4 B{HB}", hb,
           lib.lowbit_hadamard_unpack_dequant,
-          (P(c.data_ptr()), P(s.data_ptr()), N, ctypes.byref(qh), P(yh.data_ptr()), sh))
+          (P(c.data_ptr()), P(s.data_ptr()), N, ctypes.byref(qh), P(yh.data_ptr()), sh),
+          kname_hadamard_dequant(4, 7))
     del yh, c, s
 
     # 8 peer chunks of 32 Mi (the local-reduce configuration): stage-2 EF at
@@ -383,7 +390,8 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
     timed("reduce_requant_ef b4", f"{PEERS} x {NP} peers, b4 B128 -> b4 B128 + fp32 residual",
           (PEERS + 1) * out_bytes + 2 * NP * 4, lib.lowbit_reduce_requant_ef,
           (ctypes.cast(cp, P), ctypes.cast(sp, P), PEERS, NP, ctypes.byref(qi), ctypes.byref(qo),
-           P(resid.data_ptr()), P(oc.data_ptr()), P(os_.data_ptr()), None, sh))
+           P(resid.data_ptr()), P(oc.data_ptr()), P(os_.data_ptr()), None, sh),
+          kname_reduce(4, 4, 7, False, True))
     cp8 = (P * PEERS)(*[t.data_ptr() for t in pc8])
     sp8 = (P * PEERS)(*[t.data_ptr() for t in ps8])
     qi8 = qp(8, 512)
@@ -391,7 +399,8 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
     timed("reduce_requant b8->b4", f"{PEERS} x {NP} peers, b8 B512 -> b4 B128",
           PEERS * in8 + out_bytes, lib.lowbit_reduce_requant,
           (ctypes.cast(cp8, P), ctypes.cast(sp8, P), PEERS, NP, ctypes.byref(qi8),
-           ctypes.byref(qo), P(oc.data_ptr()), P(os_.data_ptr()), None, sh))
+           ctypes.byref(qo), P(oc.data_ptr()), P(os_.data_ptr()), None, sh),
+          kname_reduce(8, 4, 7, False))
     torch.cuda.synchronize()
     return out
 
