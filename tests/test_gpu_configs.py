@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times.  The oracle checks whole buffers where it finishes in
 seconds (2^20 roundtrip, the 64 Mi gradient bucket at four bitwidths, the
-8 x 32 Mi local reduce) and sampled blocks elsewhere (5-step error feedback on
-128 Mi bfloat16 gradients, the 840 Mi bfloat16 weight shard).  Sampled blocks
+8 x 32 Mi local reduce, and the extension workloads) and sampled blocks
+elsewhere (5-step error feedback on 128 Mi bfloat16 gradients, the 840 Mi
+bfloat16 weight shard).  Sampled blocks
 are recomputed by the oracle from the same host inputs with the block's global
 index offset, so the stochastic rounding sees the same counters.
 """
@@ -161,3 +162,80 @@ def test_weight_difference_840mi_bf16_b4_B64():
         assert sn[k] == ws[0], f"scale block {k}"
         assert_same(on[lo:lo + B], O.wdiff_apply(w_prev[lo:lo + B], wc, ws, bits, B),
                     f"apply block {k}")
+
+
+# ------------------------------------------------ extension rows, full size --
+# The workloads `bench.py` times for the extension kernels, in the same launch
+# configuration, checked against the oracle on whole buffers.
+
+def test_ef21_bucket_64mi_b4_B256_sr_two_steps(bucket):
+    x, gx = bucket
+    n = x.size
+    h_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    h_ref = np.zeros(n, np.float32)
+    for step in range(2):
+        say(f"ef21 64Mi fp32 b4 B256 SR seed {42 + step} step {step}")
+        c, s = L.ef21_compress(gx, h_gpu, 4, 256, True, 42 + step, 0)
+        torch.cuda.synchronize()
+        wc, ws, h_ref = O.ef21_compress(x, h_ref, 4, 256, True, 42 + step, 0)
+        assert_same(scales_np(s), ws, f"scales step {step}")
+        assert_same(codes_np(c), wc, f"codes step {step}")
+        assert_same(f32_np(h_gpu), h_ref, f"state step {step}")
+
+
+def test_hadamard_bucket_64mi_b4_B128_sr(bucket):
+    x, gx = bucket
+    n = x.size
+    say("hadamard compress 64Mi fp32 b4 B128 SR seed 42")
+    c, s = L.hadamard_quantize_pack(gx, 4, 128, True, 42, 0)
+    y = L.hadamard_unpack_dequant(c, s, n, 4, 128)
+    torch.cuda.synchronize()
+    wc, ws = O.hadamard_quantize_pack(x, 4, 128, True, 42, 0)
+    assert_same(scales_np(s), ws, "scales")
+    assert_same(codes_np(c), wc, "codes")
+    assert_same(f32_np(y), O.hadamard_unpack_dequant(wc, ws, n, 4, 128), "values")
+
+
+@pytest.fixture(scope="module")
+def peers_32mi():
+    say("generating 8 peer chunks of 32 Mi")
+    return [synth.peer_input(p) for p in range(8)]
+
+
+def _peer_codes(xs, bits, block):
+    host, dev = [], []
+    for x in xs:
+        c, s = O.quantize_pack(x, bits, block)
+        host.append((c, s))
+        dev.append((torch.from_numpy(c.view(np.int32)).cuda(),
+                    torch.from_numpy(s.view(np.float16)).cuda()))
+    return host, dev
+
+
+def test_reduce_two_level_8x32mi_b8_B512_to_b4_B128(peers_32mi):
+    n = peers_32mi[0].size
+    host, dev = _peer_codes(peers_32mi, 8, 512)
+    say("reduce 8 x 32Mi b8 B512 -> b4 B128")
+    c, s, _ = L.reduce_requant([d[0] for d in dev], [d[1] for d in dev], n, 8, 512,
+                               out_bitwidth=4, out_block_size=128)
+    torch.cuda.synchronize()
+    wc, ws, _, _ = O.reduce_requant_ex([h[0] for h in host], [h[1] for h in host], n, 8, 512, 4,
+                                       128)
+    assert_same(scales_np(s), ws, "scales")
+    assert_same(codes_np(c), wc, "codes")
+
+
+def test_reduce_stage2_ef_8x32mi_b4_B128_two_rounds(peers_32mi):
+    n = peers_32mi[0].size
+    host, dev = _peer_codes(peers_32mi, 4, 128)
+    e_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    e_ref = np.zeros(n, np.float32)
+    for rnd in range(2):
+        say(f"reduce + stage-2 EF 8 x 32Mi b4 B128 round {rnd}")
+        c, s, _ = L.reduce_requant_ef([d[0] for d in dev], [d[1] for d in dev], n, 4, 128, e_gpu)
+        torch.cuda.synchronize()
+        wc, ws, _, e_ref = O.reduce_requant_ex([h[0] for h in host], [h[1] for h in host], n, 4,
+                                               128, 4, 128, residual=e_ref)
+        assert_same(scales_np(s), ws, f"scales round {rnd}")
+        assert_same(codes_np(c), wc, f"codes round {rnd}")
+        assert_same(f32_np(e_gpu), e_ref, f"residual round {rnd}")
