@@ -9,8 +9,8 @@ static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
   constexpr int ROWS = dequant_rows<APPLY>();
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
-  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles(ntrips)),
-                     dim3(kBlockThreads), 0, s, a);
+  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles<kDeqThreads>(ntrips)),
+                     dim3(kDeqThreads), 0, s, a);
   return launch_status();
 }
 
@@ -34,8 +34,8 @@ template <int BITS, int LOG2B>
 static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   const int64_t ntrips = (nrows + kHadamardRows - 1) / kHadamardRows;
-  hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>), dim3(grid_for_tiles(ntrips)),
-                     dim3(kBlockThreads), 0, s, a);
+  hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>),
+                     dim3(grid_for_tiles<kDeqThreads>(ntrips)), dim3(kDeqThreads), 0, s, a);
   return launch_status();
 }
 

@@ -47,12 +47,12 @@ __device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* 
 
 // APPLY: 0 = decompress to binary32; 1 = weight-difference apply.
 template <int BITS, int APPLY, int DT>
-__global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
+__global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
   constexpr int E = Grid<BITS>::E;              // codes per word
   constexpr int kDequantRows = dequant_rows<APPLY>();
   const int lane = lane_id();
-  const int64_t wave = global_wave_id();
-  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t wave = global_wave_id<kDeqThreads>();
+  const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t n = a.n;
   const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
 
@@ -122,15 +122,15 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(DequantArgs a) {
 constexpr int kHadamardRows = 8;
 
 template <int BITS, int LOG2B>
-__global__ __launch_bounds__(kBlockThreads) void hadamard_dequant_kernel(DequantArgs a) {
+__global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
   constexpr int E = Grid<BITS>::E;
   constexpr int B = 1 << LOG2B;
   static_assert(B <= kHadamardRows * kDeqRow, "a block must fit in one trip");
   constexpr int LANES = B >= kDeqRow ? kWave : B / 4;
   constexpr int ROWS_PER_BLOCK = B >= kDeqRow ? B / kDeqRow : 1;
   const int lane = lane_id();
-  const int64_t wave = global_wave_id();
-  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t wave = global_wave_id<kDeqThreads>();
+  const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t n = a.n;
   const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
   const uint32_t lo = 4u * (uint32_t)lane;

@@ -16,6 +16,12 @@ constexpr int kWave = 64;
 #define LOWBIT_BLOCK_THREADS 256
 #endif
 constexpr int kBlockThreads = LOWBIT_BLOCK_THREADS;   // threads per workgroup
+// the decompress kernels' workgroup size (stores dominate; smaller groups
+// start and retire in finer steps)
+#ifndef LOWBIT_DEQ_BLOCK_THREADS
+#define LOWBIT_DEQ_BLOCK_THREADS 128
+#endif
+constexpr int kDeqThreads = LOWBIT_DEQ_BLOCK_THREADS;
 #ifndef LOWBIT_XCD_REMAP
 #define LOWBIT_XCD_REMAP 0
 #endif
@@ -86,7 +92,9 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Index of this wave in the grid, as a wave-uniform (scalar) value: element
 // offsets then split into a scalar base and a 32-bit per-lane offset, and
-// loads and stores use the scalar-base addressing mode.
+// loads and stores use the scalar-base addressing mode.  THREADS: the
+// kernel's workgroup size.
+template <int THREADS = kBlockThreads>
 __device__ __forceinline__ int64_t global_wave_id() {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   int64_t b = blockIdx.x;
@@ -99,7 +107,7 @@ __device__ __forceinline__ int64_t global_wave_id() {
     const int64_t x = b % kXcds, i = b / kXcds;
     b = x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
   }
-  return b * (kBlockThreads / kWave) + w;
+  return b * (THREADS / kWave) + w;
 }
 
 template <int CTRL>

@@ -27,8 +27,9 @@ int device_cu_count();
 // Grid for a kernel where each wave takes `ntrips` trips' worth of work: one
 // wave per trip (4 per workgroup); the kernels loop over whatever a cap
 // leaves.  The grid stays below 2^31 workgroups.
+template <int THREADS = kBlockThreads>
 inline int grid_for_tiles(int64_t ntrips) {
-  const int64_t waves_per_block = kBlockThreads / kWave;
+  const int64_t waves_per_block = THREADS / kWave;
   int64_t blocks = (ntrips + waves_per_block - 1) / waves_per_block;
   int64_t cap = (int64_t)1 << 30;
   if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;

@@ -27,11 +27,20 @@ namespace lowbit {
 #define LOWBIT_HS_ELEMS_PER_TRIP 32
 #endif
 
+// Error-feedback compresses read two streams and write one; a single tile
+// per trip keeps their register use and per-wave footprint small.
+#ifndef LOWBIT_EF_ELEMS_PER_TRIP
+#define LOWBIT_EF_ELEMS_PER_TRIP 8
+#endif
+
 // Tiles per trip of the compress kernel for a tile of PER_LANE elements per
 // lane, by rounding, input type and mode.
 template <int PER_LANE, bool SR, int DT, int MODE>
 constexpr int compress_tiles_per_trip() {
-  if constexpr (MODE == kHadamard) {
+  if constexpr (MODE == kErrorFeedback || MODE == kEF21) {
+    constexpr int want = LOWBIT_EF_ELEMS_PER_TRIP;
+    return PER_LANE >= want ? 1 : want / PER_LANE;
+  } else if constexpr (MODE == kHadamard) {
     constexpr int want = LOWBIT_HS_ELEMS_PER_TRIP;
     return PER_LANE >= want ? 1 : want / PER_LANE;
   } else {
