@@ -349,3 +349,18 @@ def test_hadamard_rejects_partial_blocks(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.hadamard_unpack_dequant(np.zeros(25, np.uint32), np.zeros(2, np.uint16), 200,
                                            4, 128)
+
+
+def test_hadamard_handworked_stage_order(oracle_mod):
+    """Worked by hand: B = 32, x = [1, 2^-24, -1, 2^-24, 0, ..., 0].
+    Stride 1: fl(1 + 2^-24) = 1 (tie, to even), fl(1 - 2^-24) = 1 - 2^-24
+    (exact), fl(-1 + 2^-24) = -1 + 2^-24 (exact), fl(-1 - 2^-24) = -1 (tie).
+    Stride 2: y0 = 1 + (-1 + 2^-24) = 2^-24, y1 = (1 - 2^-24) + (-1) = -2^-24,
+    y2 = 1 - (-1 + 2^-24) = 2 - 2^-24 -> 2 (tie, to even), y3 = (1 - 2^-24) -
+    (-1) -> 2.  Strides 4..16 pair these with zeros and copy them, so the
+    block is [2^-24, -2^-24, 2, 2] eight times, scaled by 2^-floor(5/2) = 1/4.
+    The strides in the other order would give y0 = (1 - 1) + 2^-23 = 2^-23."""
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[2], x[3] = 1.0, 2.0 ** -24, -1.0, 2.0 ** -24
+    want = np.tile(np.array([2.0 ** -26, -2.0 ** -26, 0.5, 0.5], np.float32), 8)
+    assert np.array_equal(oracle_mod.hadamard_blocks(x, 32), want)
