@@ -292,18 +292,37 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
 // in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16).
-template <int DT, int E>
+// Non-temporal loads in the error-feedback compresses: 0 none, 1 the
+// residual/state (rewritten in place), 2 the gradient too.  Measured on the
+// 64 Mi bucket step: with 1, the EF compress no longer leaves dirty residual
+// lines in the Infinity Cache (the kernel after it runs 15 us faster) but is
+// itself 18 us slower (149 vs 131 us); the step gains 1 %.  0 keeps the EF
+// compress, the largest kernel of the step, at its own best rate.
+#ifndef LOWBIT_EF_NT_LOADS
+#define LOWBIT_EF_NT_LOADS 0
+#endif
+typedef float f32x4l __attribute__((ext_vector_type(4)));
+
+template <int DT, int E, bool NT = false>
 __device__ __forceinline__ void load_vec(const void* base, int64_t t0, uint32_t off, float* v) {
   if constexpr (DT == kF32) {
     const float* p = static_cast<const float*>(base) + t0;
     const float4* q = reinterpret_cast<const float4*>(p + off);
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-      float4 t = q[k];
-      v[4 * k + 0] = t.x;
-      v[4 * k + 1] = t.y;
-      v[4 * k + 2] = t.z;
-      v[4 * k + 3] = t.w;
+      if constexpr (NT) {
+        const f32x4l t = __builtin_nontemporal_load(reinterpret_cast<const f32x4l*>(q) + k);
+        v[4 * k + 0] = t.x;
+        v[4 * k + 1] = t.y;
+        v[4 * k + 2] = t.z;
+        v[4 * k + 3] = t.w;
+      } else {
+        float4 t = q[k];
+        v[4 * k + 0] = t.x;
+        v[4 * k + 1] = t.y;
+        v[4 * k + 2] = t.z;
+        v[4 * k + 3] = t.w;
+      }
     }
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + t0;

@@ -178,8 +178,9 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
     const uint32_t off = (uint32_t)(r * kWave + lane) * E;
     float w[E];
     if constexpr (FULL) {
-      load_vec<DT, E>(a.x, t0, off, v[r]);
-      if constexpr (MODE == kErrorFeedback || MODE == kEF21) load_vec<kF32, E>(a.resid, t0, off, w);
+      constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
+      load_vec<DT, E, RMW && LOWBIT_EF_NT_LOADS >= 2>(a.x, t0, off, v[r]);
+      if constexpr (RMW) load_vec<kF32, E, LOWBIT_EF_NT_LOADS >= 1>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, t0, off, w);
     } else {
       load_tail<DT, E>(a.x, t0, off, a.n - t0, v[r]);
