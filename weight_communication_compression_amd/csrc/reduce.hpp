@@ -95,88 +95,88 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
 // scalar loads).  G is 8, fewer when a lane's share of a trip is large, so
 // that at most 32 loaded words per lane are held at once.  GUARD: some slots
 // of the trip lie past the end of the buffer (read as 0).
+#ifndef LOWBIT_PEER_GROUP
+#define LOWBIT_PEER_GROUP 8
+#endif
 template <int W, int M>
 constexpr int peer_group() {
-  return 32 / (W * M) >= 8 ? 8 : (32 / (W * M) >= 1 ? 32 / (W * M) : 1);
+  constexpr int G = LOWBIT_PEER_GROUP;
+  return 32 / (W * M) >= G ? G : (32 / (W * M) >= 1 ? 32 / (W * M) : 1);
 }
 
-template <int IN_BITS, int BITS, int R, int W, bool GUARD>
-__device__ __forceinline__ void reduce_peers(const ReduceArgs& a, const int64_t* wt,
-                                             const int64_t* kt, const uint32_t* wl,
-                                             const uint32_t* kl, const bool* in,
-                                             float (*acc)[Grid<BITS>::E]) {
+// Loads of peers g .. g+G-1 (those below npeers) for the W slots of a trip.
+template <int IN_BITS, int BITS, int R, int W, int G, bool GUARD>
+__device__ __forceinline__ void load_peer_group(const ReduceArgs& a, int g, const int64_t* wt,
+                                                const int64_t* kt, const uint32_t* wl,
+                                                const uint32_t* kl, const bool* in,
+                                                uint32_t (*w)[W][in_words<IN_BITS, BITS>()],
+                                                uint32_t (*sc)[W]) {
   constexpr int M = in_words<IN_BITS, BITS>();
-  constexpr int EIN = Grid<IN_BITS>::E;
-  constexpr int kPeerGroup = peer_group<W, M>();
   const int np = a.npeers;
   const int64_t nwin = (a.n * IN_BITS + 31) / 32;       // input words per peer
   (void)nwin;
-#pragma unroll 1
-  for (int g = 0; g < np; g += kPeerGroup) {
-    uint32_t w[kPeerGroup][W][M], sc[kPeerGroup][W];
 #pragma unroll
-    for (int q = 0; q < kPeerGroup; ++q) {
-      if (g + q < np) {                                   // wave-uniform
-        const uint32_t* cp = a.codes[g + q];
-        const uint16_t* sp = a.scales[g + q];
+  for (int q = 0; q < G; ++q) {
+    if (g + q < np) {                                   // wave-uniform
+      const uint32_t* cp = a.codes[g + q];
+      const uint16_t* sp = a.scales[g + q];
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-          if (GUARD) {
-            // word by word: the last output word's input words may end early
-            const int64_t w0 = wt[i / R] + (int64_t)wl[i] * M;
+      for (int i = 0; i < W; ++i) {
+        if (GUARD) {
+          // word by word: the last output word's input words may end early
+          const int64_t w0 = wt[i / R] + (int64_t)wl[i] * M;
 #pragma unroll
-            for (int m = 0; m < M; ++m) w[q][i][m] = (in[i] && w0 + m < nwin) ? cp[w0 + m] : 0u;
-            sc[q][i] = in[i] ? (sp + kt[i / R])[kl[i]] : 0u;
-          } else {
-            load_words<M>(cp + wt[i / R] + wl[i] * M, w[q][i]);
-            sc[q][i] = (sp + kt[i / R])[kl[i]];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kPeerGroup; ++q) {
-      if (g + q < np) {
-#pragma unroll
-        for (int i = 0; i < W; ++i) {
-          const float s = f16_bits_to_f32(sc[q][i]);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            if (q == 0 && g == 0) accumulate_word<IN_BITS, true>(w[q][i][m], s, acc[i] + m * EIN);
-            else accumulate_word<IN_BITS, false>(w[q][i][m], s, acc[i] + m * EIN);
-          }
+          for (int m = 0; m < M; ++m) w[q][i][m] = (in[i] && w0 + m < nwin) ? cp[w0 + m] : 0u;
+          sc[q][i] = in[i] ? (sp + kt[i / R])[kl[i]] : 0u;
+        } else {
+          load_words<M>(cp + wt[i / R] + wl[i] * M, w[q][i]);
+          sc[q][i] = (sp + kt[i / R])[kl[i]];
         }
       }
     }
   }
 }
 
-// Reduce and requantize NT consecutive output tiles starting at tile `tile0`.
-// GUARD: the tiles may reach past the end of the buffer (only in the tail
-// kernel): loads past the end read 0 and those positions are +0 for the
-// statistic.  EF: stage-2 error feedback with the residual a.resid.
-template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD>
-__device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0) {
-  using S = TileShape<BITS, LOG2B>;
-  constexpr int E = S::E, R = S::R, W = NT * R;
+// Decode loaded peers g .. g+G-1 into acc, in peer order (peer 0 starts the
+// sums).
+template <int IN_BITS, int BITS, int W, int G>
+__device__ __forceinline__ void decode_peer_group(const ReduceArgs& a, int g,
+                                                  const uint32_t (*w)[W][in_words<IN_BITS, BITS>()],
+                                                  const uint32_t (*sc)[W],
+                                                  float (*acc)[Grid<BITS>::E]) {
   constexpr int M = in_words<IN_BITS, BITS>();
-  constexpr int K = acc_shift<IN_BITS>();
-  constexpr float UNSCALE = 1.0f / (float)(1 << K);              // exact
-  // the statistic can absorb the 2^K of the sums unless it is the 1-bit mean
-  // or a residual is added first
-  constexpr bool UNSCALE_FIRST = EF || (BITS == 1 && K > 0);
-  const int lane = lane_id();
-  const int64_t n = a.n;
-  const int64_t nwords = (n + E - 1) / E;           // output words
-  const int lbi = a.in_log2b;
+  constexpr int EIN = Grid<IN_BITS>::E;
+  const int np = a.npeers;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    if (g + q < np) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const float s = f16_bits_to_f32(sc[q][i]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          if (q == 0 && g == 0) accumulate_word<IN_BITS, true>(w[q][i][m], s, acc[i] + m * EIN);
+          else accumulate_word<IN_BITS, false>(w[q][i][m], s, acc[i] + m * EIN);
+        }
+      }
+    }
+  }
+}
 
-  // slot i = (tile u, row r): the tile's first input word and input block
-  // are wave-uniform; the lane's output word and input block within the tile
-  // are 32-bit.  A tile either lies inside one input block or starts on a
-  // block boundary, so block(t0 + off) = block(t0) + (off >> lbi).
-  int64_t wt[NT], kt[NT];
-  uint32_t wl[W], kl[W];
-  bool in[W];
+// Slot addressing of a trip of NT output tiles from `tile0`: slot i = (tile
+// u, row r); the tile's first input word and input block are wave-uniform,
+// the lane's output word and input block within the tile are 32-bit.  A tile
+// either lies inside one input block or starts on a block boundary, so
+// block(t0 + off) = block(t0) + (off >> in_log2b).
+template <int IN_BITS, int BITS, int LOG2B, int NT, bool GUARD>
+__device__ __forceinline__ void trip_slots(const ReduceArgs& a, int64_t tile0, int64_t* wt,
+                                           int64_t* kt, uint32_t* wl, uint32_t* kl, bool* in) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R;
+  constexpr int M = in_words<IN_BITS, BITS>();
+  const int lane = lane_id();
+  const int64_t nwords = (a.n + E - 1) / E;           // output words
+  const int lbi = a.in_log2b;
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int64_t t0 = (tile0 + u) * S::TILE;
@@ -190,25 +190,45 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
       in[u * R + r] = !GUARD || t0 / E + w < nwords;
     }
   }
+}
 
-  // stage-2 residual of the lane's elements, in flight with the first peers
-  float e[NT][R][E];
-  if constexpr (EF) {
+// The stage-2 residual of the lane's elements of NT tiles from `tile0`.
+template <int BITS, int LOG2B, int NT, bool GUARD>
+__device__ __forceinline__ void load_residual(
+    const ReduceArgs& a, int64_t tile0,
+    float (*e)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R;
+  const int lane = lane_id();
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const int64_t t0 = (tile0 + u) * S::TILE;
+  for (int u = 0; u < NT; ++u) {
+    const int64_t t0 = (tile0 + u) * S::TILE;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t off = (uint32_t)(r * kWave + lane) * E;
-        if (!GUARD || t0 + S::TILE <= n) load_vec<kF32, E>(a.resid, t0, off, e[u][r]);
-        else load_tail<kF32, E>(a.resid, t0, off, n - t0, e[u][r]);
-      }
+    for (int r = 0; r < R; ++r) {
+      const uint32_t off = (uint32_t)(r * kWave + lane) * E;
+      if (!GUARD || t0 + S::TILE <= a.n) load_vec<kF32, E>(a.resid, t0, off, e[u][r]);
+      else load_tail<kF32, E>(a.resid, t0, off, a.n - t0, e[u][r]);
     }
   }
+}
 
-  float acc[NT][R][E];
-  reduce_peers<IN_BITS, BITS, R, W, GUARD>(a, wt, kt, wl, kl, in, &acc[0][0]);
-
+// From the peer sums of NT tiles (scaled by 2^acc_shift<IN_BITS>): zero the
+// positions past the end, write the optional sum, add the residual (EF),
+// requantize, and write the new residual (EF).
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD>
+__device__ __forceinline__ void requant_tiles(
+    const ReduceArgs& a, int64_t tile0,
+    float (*acc)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E],
+    const float (*e)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R;
+  constexpr int K = acc_shift<IN_BITS>();
+  constexpr float UNSCALE = 1.0f / (float)(1 << K);              // exact
+  // the statistic can absorb the 2^K of the sums unless it is the 1-bit mean
+  // or a residual is added first
+  constexpr bool UNSCALE_FIRST = EF || (BITS == 1 && K > 0);
+  const int lane = lane_id();
+  const int64_t n = a.n;
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int64_t t0 = (tile0 + u) * S::TILE;
@@ -218,7 +238,7 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < E; ++j)
-          if (t0 + (int64_t)wl[u * R + r] * E + j >= n) acc[u][r][j] = 0.0f;
+          if (t0 + (int64_t)(r * kWave + lane) * E + j >= n) acc[u][r][j] = 0.0f;
     }
     if (a.out_sum) {
 #pragma unroll
@@ -261,9 +281,41 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
   (void)e;
 }
 
+// Reduce and requantize NT consecutive output tiles starting at tile `tile0`,
+// any number of peers (groups of G: all loads of a group are issued before
+// any of its peers is decoded).  GUARD: the tiles may reach past the end of
+// the buffer (only in the tail kernel): loads past the end read 0 and those
+// positions are +0 for the statistic.  EF: stage-2 error feedback with the
+// residual a.resid.
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD>
+__device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int E = S::E, R = S::R, W = NT * R;
+  constexpr int M = in_words<IN_BITS, BITS>();
+  constexpr int G = peer_group<W, M>();
+  int64_t wt[NT], kt[NT];
+  uint32_t wl[W], kl[W];
+  bool in[W];
+  trip_slots<IN_BITS, BITS, LOG2B, NT, GUARD>(a, tile0, wt, kt, wl, kl, in);
+  // stage-2 residual of the lane's elements, in flight with the first peers
+  float e[NT][R][E];
+  if constexpr (EF) load_residual<BITS, LOG2B, NT, GUARD>(a, tile0, e);
+  float acc[NT][R][E];
+#pragma unroll 1
+  for (int g = 0; g < a.npeers; g += G) {
+    uint32_t w[G][W][M], sc[G][W];
+    load_peer_group<IN_BITS, BITS, R, W, G, GUARD>(a, g, wt, kt, wl, kl, in, w, sc);
+    decode_peer_group<IN_BITS, BITS, W, G>(a, g, w, sc, &acc[0][0]);
+  }
+  requant_tiles<IN_BITS, BITS, LOG2B, SR, EF, NT, GUARD>(a, tile0, acc, e);
+}
+
 // Main kernel (TAIL = false): each wave takes one trip of U full tiles; the
 // grid covers the complete trips of full tiles only (`first` = number of full
 // tiles).  Tail kernel (TAIL = true, one wave): tiles from `first` on.
+// (Measured: a grid of a few workgroups per CU whose waves walk several trips
+// and issue the next trip's loads before decoding the current one is 30 %
+// slower on 8 x 32 Mi peers than one trip per wave.)
 template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL>
 __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
