@@ -7,7 +7,8 @@ namespace lowbit {
 template <int BITS, int APPLY, int DT>
 static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
   constexpr int ROWS = dequant_rows<APPLY>();
-  const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
+  constexpr int ROW = kWave * dequant_epl<APPLY>();
+  const int64_t nrows = (a.n + ROW - 1) / ROW;
   const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
   hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles<kDeqThreads>(ntrips)),
                      dim3(kDeqThreads), 0, s, a);

@@ -15,95 +15,129 @@
 
 namespace lowbit {
 
-// rows per lane per loop trip: decompress writes 16 B per row and lane,
-// apply also reads 8-16 B, so it keeps fewer rows in flight
+// rows per lane per loop trip, and elements per lane per row (decompress:
+// 4, a 16-byte binary32 store; apply: 8, a 16-byte bfloat16 load and store)
 #ifndef LOWBIT_DEQ_ROWS
 #define LOWBIT_DEQ_ROWS 8
 #endif
 #ifndef LOWBIT_APPLY_ROWS
 #define LOWBIT_APPLY_ROWS 2
 #endif
+#ifndef LOWBIT_DEQ_EPL
+#define LOWBIT_DEQ_EPL 4
+#endif
+#ifndef LOWBIT_APPLY_EPL
+#define LOWBIT_APPLY_EPL 8
+#endif
 template <int APPLY>
 constexpr int dequant_rows() { return APPLY ? LOWBIT_APPLY_ROWS : LOWBIT_DEQ_ROWS; }
-constexpr int kDeqRow = kWave * 4;              // elements per row
+template <int APPLY>
+constexpr int dequant_epl() { return APPLY ? LOWBIT_APPLY_EPL : LOWBIT_DEQ_EPL; }
+constexpr int kDeqRow = kWave * 4;              // elements per row at 4 per lane
 
-// Decode the 4 codes in bits [off, off + 4b) of `word` with scale s.
-template <int BITS>
-__device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* d) {
+// Decode the N codes in bits [off, off + N*b) of `word` with scale s
+// (N * b <= 32).
+template <int BITS, int N>
+__device__ __forceinline__ void decode_n(uint32_t word, int off, float s, float* d) {
   using G = Grid<BITS>;
   const uint32_t piece = word >> off;
   if constexpr (BITS == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[j] = signed_scale(piece, j, s);
+    for (int j = 0; j < N; ++j) d[j] = signed_scale(piece, j, s);
   } else {
     const uint32_t tw = piece ^ G::FLIP;        // fields become two's-complement q
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < N; ++j) {
       const int q = (int)(tw << (32 - BITS * (j + 1))) >> (32 - BITS);
       d[j] = (float)q * s;                      // exact
     }
   }
 }
 
-// APPLY: 0 = decompress to binary32; 1 = weight-difference apply.
+template <int BITS>
+__device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* d) {
+  decode_n<BITS, 4>(word, off, s, d);
+}
+
+// APPLY: 0 = decompress to binary32; 1 = weight-difference apply.  Element-
+// centric: a row is 64 * EPL consecutive elements, lane l decodes elements
+// EPL*l .. EPL*l + EPL - 1 (their codes are EPL*b consecutive bits of one
+// word, or two words for 8 codes of 8 bits); blocks are >= 32 elements, so
+// each lane needs one scale.
 template <int BITS, int APPLY, int DT>
 __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
   constexpr int E = Grid<BITS>::E;              // codes per word
   constexpr int kDequantRows = dequant_rows<APPLY>();
+  constexpr int EPL = dequant_epl<APPLY>();
+  constexpr int ROW = kWave * EPL;
+  constexpr int NW = EPL * BITS > 32 ? EPL * BITS / 32 : 1;   // words per lane
+  constexpr int LOG2ROW = EPL == 8 ? 9 : 8;
+  static_assert(ROW == 1 << LOG2ROW, "rows of 256 or 512 elements");
   const int lane = lane_id();
   const int64_t wave = global_wave_id<kDeqThreads>();
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t n = a.n;
-  const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
+  const int64_t nrows = (n + ROW - 1) / ROW;
 
   for (int64_t base = wave * kDequantRows; base < nrows; base += nwaves * kDequantRows) {
-    uint32_t word[kDequantRows];
+    uint32_t word[kDequantRows][NW];
     uint32_t s16[kDequantRows];
-    float wo[kDequantRows][4];
-    const uint32_t lo = 4u * (uint32_t)lane;                  // lane's element within a row
+    float wo[kDequantRows][EPL];
+    const uint32_t lo = (uint32_t)EPL * (uint32_t)lane;       // lane's element within a row
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t r0 = (base + r) * kDeqRow;                // row start (wave-uniform)
-      word[r] = 0;
+      const int64_t r0 = (base + r) * ROW;                    // row start (wave-uniform)
+#pragma unroll
+      for (int k = 0; k < NW; ++k) word[r][k] = 0;
       s16[r] = 0;
       if (r0 + lo < n) {
-        word[r] = (a.codes + r0 / E)[lo / E];
-        // blocks of >= 256 elements cover the whole row: one scale per row
-        s16[r] = a.log2b >= 8 ? a.scales[r0 >> a.log2b]
-                              : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
+        const uint32_t* cw = a.codes + r0 / E;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) word[r][k] = cw[lo / E + k];
+        // blocks of >= ROW elements cover the whole row: one scale per row
+        s16[r] = a.log2b >= LOG2ROW ? a.scales[r0 >> a.log2b]
+                                    : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
         if constexpr (APPLY) {
-          if (r0 + lo + 4 <= n) load_vec<DT, 4>(a.w_old, r0, lo, wo[r]);
-          else load_tail<DT, 4>(a.w_old, r0, lo, n - r0, wo[r]);
+          if (r0 + lo + EPL <= n) load_vec<DT, EPL>(a.w_old, r0, lo, wo[r]);
+          else load_tail<DT, EPL>(a.w_old, r0, lo, n - r0, wo[r]);
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t r0 = (base + r) * kDeqRow;
+      const int64_t r0 = (base + r) * ROW;
       if (r0 + lo >= n) continue;
-      float d[4];
-      decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d);
-      const bool full = r0 + lo + 4 <= n;
-      if constexpr (!APPLY) {
-        if (full) store_vec_f32<4>(a.y, r0, lo, d);
-        else store_tail_f32<4>(a.y, r0, lo, n - r0, d);
+      float d[EPL];
+      const float s = f16_bits_to_f32(s16[r]);
+      if constexpr (NW == 1) {
+        decode_n<BITS, EPL>(word[r][0], (int)(lo % E) * BITS, s, d);
       } else {
-        float w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = wo[r][j] + d[j];
+        for (int k = 0; k < NW; ++k) decode_n<BITS, E>(word[r][k], 0, s, d + k * E);
+      }
+      const bool full = r0 + lo + EPL <= n;
+      if constexpr (!APPLY) {
+        if (full) store_vec_f32<EPL>(a.y, r0, lo, d);
+        else store_tail_f32<EPL>(a.y, r0, lo, n - r0, d);
+      } else {
+        float w[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) w[j] = wo[r][j] + d[j];
         if constexpr (DT == kF32) {
-          if (full) store_vec_f32<4>(static_cast<float*>(a.w_out), r0, lo, w);
-          else store_tail_f32<4>(static_cast<float*>(a.w_out), r0, lo, n - r0, w);
+          if (full) store_vec_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, w);
+          else store_tail_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, n - r0, w);
         } else {
           const int64_t e0 = r0 + lo;
           uint16_t* out = static_cast<uint16_t*>(a.w_out) + r0 + lo;
           if (full) {
-            store_stream(reinterpret_cast<uint2*>(out),
-                         make_uint2(f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16),
-                                    f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16)));
+            uint32_t pk[EPL / 2];
+#pragma unroll
+            for (int k = 0; k < EPL / 2; ++k)
+              pk[k] = f32_to_bf16_rne(w[2 * k]) | (f32_to_bf16_rne(w[2 * k + 1]) << 16);
+            store_stream_words<EPL / 2>(reinterpret_cast<uint32_t*>(out), pk);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < EPL; ++j)
               if (e0 + j < n) out[j] = (uint16_t)f32_to_bf16_rne(w[j]);
           }
         }

@@ -376,13 +376,17 @@ __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) {
   if (LOWBIT_NT_STORES) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
-__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
-  if (LOWBIT_NT_STORES) {
-    const u32x2 q = {v.x, v.y};
-    __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(p));
-  } else {
-    *p = v;
-  }
+
+// K = 2 or 4 words (8 or 16 bytes, aligned to that) in one streaming store.
+template <int K>
+__device__ __forceinline__ void store_stream_words(uint32_t* p, const uint32_t* v) {
+  static_assert(K == 2 || K == 4, "8- or 16-byte stores");
+  typedef uint32_t vk __attribute__((ext_vector_type(K)));
+  vk q;
+#pragma unroll
+  for (int k = 0; k < K; ++k) q[k] = v[k];
+  if (LOWBIT_NT_STORES) __builtin_nontemporal_store(q, reinterpret_cast<vk*>(p));
+  else *reinterpret_cast<vk*>(p) = q;
 }
 
 template <int E>
