@@ -1,12 +1,14 @@
-// dequant.hpp -- decompress kernels: codes + scales -> binary32, and the
-// weight-difference apply w_out = to_dtype(w_old + deq).
+// dequant.hpp -- decompress kernels: codes + scales -> binary32, the
+// weight-difference apply w_out = to_dtype(w_old + deq), and the decompress
+// with inverse Hadamard smoothing.
 //
-// Element-centric layout: a "row" is 256 consecutive elements and lane l of a
-// wave decodes elements 4l .. 4l+3 of it, so every binary32 (or bfloat16)
-// store of the wave is one fully coalesced 1 KiB (512 B) access at any
-// bitwidth.  The 4 codes of a lane are 4b consecutive bits of one packed word
-// (lanes sharing a word read the same address, served by the cache), and a
-// word never straddles a block (B >= 32), so each lane needs one scale.
+// Element-centric layout: a "row" is 64 * EPL consecutive elements and lane l
+// of a wave decodes elements EPL*l .. EPL*l + EPL-1 of it (EPL = 4 for the
+// decompress, 8 for the apply), so every binary32 or bfloat16 store of the
+// wave is one fully coalesced access at any bitwidth.  The codes of a lane are
+// consecutive bits of one packed word (two for 8 codes of 8 bits; lanes
+// sharing a word read the same address, served by the cache), and blocks are
+// at least 32 elements, so each lane needs one scale.
 #pragma once
 
 #include "args.hpp"

@@ -79,10 +79,11 @@ constexpr int tiles_per_trip() {
   return PER_LANE >= want ? 1 : want / PER_LANE;
 }
 
-// Non-temporal hint on the large binary32 outputs (decompressed values,
-// residuals, sums, applied weights): written through rather than parked dirty
-// in the Infinity Cache, where the next kernel would pay for their write-back
-// (measured: +12 % on a whole compress/reduce/decompress/EF/weight-diff pass).
+// Non-temporal hint on the large outputs (decompressed values, residuals,
+// sums, packed codes, applied weights): written through rather than parked
+// dirty in the Infinity Cache, where the next kernel would pay for their
+// write-back (measured: +12 % on a whole compress/reduce/decompress/EF/
+// weight-diff pass).
 #ifndef LOWBIT_NT_STORES
 #define LOWBIT_NT_STORES 1
 #endif
@@ -290,8 +291,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // element offset `off`, which maps onto the scalar-base + 32-bit-offset
 // addressing mode of global loads and stores.
 
-// Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
-// in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16).
 // Non-temporal loads in the error-feedback compresses: 0 none, 1 the
 // residual/state (rewritten in place), 2 the gradient too.  Measured on the
 // 64 Mi bucket step: with 1, the EF compress no longer leaves dirty residual
@@ -301,8 +300,11 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 #ifndef LOWBIT_EF_NT_LOADS
 #define LOWBIT_EF_NT_LOADS 0
 #endif
-typedef float f32x4l __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
+// in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16); NT: non-temporal
+// (binary32 only).
 template <int DT, int E, bool NT = false>
 __device__ __forceinline__ void load_vec(const void* base, int64_t t0, uint32_t off, float* v) {
   if constexpr (DT == kF32) {
@@ -311,7 +313,7 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t t0, uint32_t 
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
       if constexpr (NT) {
-        const f32x4l t = __builtin_nontemporal_load(reinterpret_cast<const f32x4l*>(q) + k);
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q) + k);
         v[4 * k + 0] = t.x;
         v[4 * k + 1] = t.y;
         v[4 * k + 2] = t.z;
@@ -365,9 +367,6 @@ __device__ __forceinline__ void load_tail(const void* base, int64_t t0, uint32_t
     v[j] = x;
   }
 }
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Streaming stores: outputs are written once and read by a later kernel, so
 // they are stored non-temporally and do not linger as dirty cache lines whose

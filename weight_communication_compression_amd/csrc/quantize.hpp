@@ -1,5 +1,6 @@
 // quantize.hpp -- blockwise compress of one tile held in registers, and the
-// compress kernel built on it (plain / error feedback / weight difference).
+// compress kernel built on it (plain, error feedback, weight difference,
+// EF21, Hadamard-smoothed).
 // Templated on bitwidth, block size, rounding, input dtype and mode so that
 // the inner loop has no run-time branches.
 //
