@@ -30,7 +30,9 @@ the same workload.
 their own workloads: EF21 compress and Hadamard-smoothed compress /
 decompress of the bucket, and the local reduce of 8 peer chunks of 32 Mi with
 stage-2 error feedback (b4 B128) and with two-level requantization (8-bit
-B512 peers to 4-bit B128).
+B512 peers to 4-bit B128).  `roundtrip_4mib` times the 2^20-element
+compress + decompress once and over a ring of 256 distinct buffers, issued
+eagerly and from a HIP graph (launch-bound at this size).
 """
 from __future__ import annotations
 
@@ -105,7 +107,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--next-rows", type=int, default=1,
-                    help="also time the extension kernels alone (1) or not (0)")
+                    help="also time the extension kernels and the 4 MiB roundtrip alone "
+                         "(1) or not (0)")
     ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="elements of the bucket the CPU oracle processes (0 = skip)")
     args = ap.parse_args()
@@ -274,6 +277,7 @@ def main() -> int:
 
     # ----------------------------------------- extensions beyond the step --
     next_rows = measure_next_rows(L, lib, dev, stream, x) if args.next_rows else None
+    roundtrip = measure_roundtrip(L, dev) if args.next_rows else None
 
     # ------------------------------------------------------- CPU oracle --
     cpu = None
@@ -299,6 +303,8 @@ def main() -> int:
     }
     if next_rows is not None:
         out["next_rows"] = next_rows
+    if roundtrip is not None:
+        out["roundtrip_4mib"] = roundtrip
     print(json.dumps(out), flush=True)
     return 0
 
@@ -403,6 +409,74 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
           kname_reduce(8, 4, 7, False))
     torch.cuda.synchronize()
     return out
+
+
+def measure_roundtrip(L, dev, reps=20, ring=256):
+    """The 2^20-element roundtrip (compress b4 B128 nearest, then decompress):
+    one launch of each is launch-bound (4.7 MB of traffic), so it is also
+    timed over a ring of `ring` distinct 4 MiB buffers (1 GiB), issued
+    eagerly and replayed from a HIP graph.  The graph's output is checked
+    against the eager output.  Not part of `value`."""
+    import torch
+
+    n, bits, block = 1 << 20, 4, 128
+    gen = torch.Generator(device=dev).manual_seed(0)
+    xs = [torch.randn(n, device=dev, generator=gen) for _ in range(ring)]
+    nw, nb = L.num_words(n, bits), L.num_blocks(n, block)
+    cs = [torch.empty(nw, dtype=torch.int32, device=dev) for _ in range(ring)]
+    ss = [torch.empty(nb, dtype=torch.float16, device=dev) for _ in range(ring)]
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(ring)]
+    per_pass = 2 * (n * 4 + nw * 4 + nb * 2)            # compress + decompress bytes
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def one(k):
+        L.quantize_pack(xs[k], bits, block, codes=cs[k], scales=ss[k])
+        L.unpack_dequant(cs[k], ss[k], n, bits, block, out=ys[k])
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    for k in range(ring):
+        one(k)
+    torch.cuda.synchronize()
+    single = timed(lambda: one(0))
+    eager = timed(lambda: [one(k) for k in range(ring)])
+    want = cs[ring - 1].clone(), ys[ring - 1].clone()
+    cs[ring - 1].zero_()
+    ys[ring - 1].zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for k in range(ring):
+                one(k)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(cs[ring - 1], want[0]) and torch.equal(ys[ring - 1], want[1])):
+        raise RuntimeError("graph replay of the roundtrip differs from the eager result")
+    replay = timed(graph.replay)
+    if not (torch.equal(cs[ring - 1], want[0]) and torch.equal(ys[ring - 1], want[1])):
+        raise RuntimeError("a later graph replay of the roundtrip differs from the eager result")
+    total = ring * per_pass
+    return {"workload": f"{n} fp32 N(0,1), b4 B128 nearest: compress + decompress",
+            "single_pass_us": round(single * 1e3, 2),
+            "single_pass_GBps": round(per_pass / (single * 1e-3) / 1e9, 1),
+            "ring": f"{ring} distinct 4 MiB buffers (1 GiB)",
+            "ring_eager_GBps": round(total / (eager * 1e-3) / 1e9, 1),
+            "ring_graph_GBps": round(total / (replay * 1e-3) / 1e9, 1),
+            "ring_graph_frac": round(total / (replay * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
 
 
 def cpu_baseline(x, w_prev, w_new, n, nstages):
