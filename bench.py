@@ -32,7 +32,10 @@ decompress of the bucket, and the local reduce of 8 peer chunks of 32 Mi with
 stage-2 error feedback (b4 B128) and with two-level requantization (8-bit
 B512 peers to 4-bit B128).  `roundtrip_4mib` times the 2^20-element
 compress + decompress once and over a ring of 256 distinct buffers, issued
-eagerly and from a HIP graph (launch-bound at this size).
+eagerly and from a HIP graph (launch-bound at this size).  `configs` times
+the kernels of the other workload configurations at full size: EF compress of
+128 Mi bfloat16 gradients, the 8 x 32 Mi local reduce, and weight-difference
+compress / apply of an 840 Mi bfloat16 shard.
 """
 from __future__ import annotations
 
@@ -278,6 +281,7 @@ def main() -> int:
     # ----------------------------------------- extensions beyond the step --
     next_rows = measure_next_rows(L, lib, dev, stream, x) if args.next_rows else None
     roundtrip = measure_roundtrip(L, dev) if args.next_rows else None
+    configs = measure_configs(L, dev) if args.next_rows else None
 
     # ------------------------------------------------------- CPU oracle --
     cpu = None
@@ -305,6 +309,8 @@ def main() -> int:
         out["next_rows"] = next_rows
     if roundtrip is not None:
         out["roundtrip_4mib"] = roundtrip
+    if configs is not None:
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
     return 0
 
@@ -407,6 +413,78 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
           (ctypes.cast(cp8, P), ctypes.cast(sp8, P), PEERS, NP, ctypes.byref(qi8),
            ctypes.byref(qo), P(oc.data_ptr()), P(os_.data_ptr()), None, sh),
           kname_reduce(8, 4, 7, False))
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_configs(L, dev, reps=20):
+    """The kernels of the other workload configurations at their full sizes,
+    each timed alone (median of `reps`, every launch after a 1 GiB read that
+    leaves the Infinity Cache clean).  Inputs are drawn on the GPU from seeded
+    generators with the configurations' distributions.  Not part of `value`."""
+    import torch
+
+    gen = torch.Generator(device=dev).manual_seed(5)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    out = {}
+
+    def timed(name, workload, alg_bytes, fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
+                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3)}
+
+    # error feedback on 128 Mi bfloat16 gradients, b4 B128 SR
+    n = 128 << 20
+    g = (torch.randn(n, device=dev, generator=gen) * 1e-4).to(torch.bfloat16)
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    c = torch.empty(L.num_words(n, 4), dtype=torch.int32, device=dev)
+    s = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
+    timed("ef_compress 128Mi bf16", f"{n} bf16 N(0,1e-4), fp32 residual, b4 B128 SR",
+          n * (2 + 4 + 4) + c.numel() * 4 + s.numel() * 2,
+          lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s))
+    del g, e, c, s
+
+    # local reduce of 8 peer chunks of 32 Mi, b4 B128 in and out
+    n = 32 << 20
+    pc, ps = [], []
+    for _ in range(8):
+        xp = torch.randn(n, device=dev, generator=gen)
+        a, b = L.quantize_pack(xp, 4, 128)
+        pc.append(a)
+        ps.append(b)
+        del xp
+    oc = torch.empty(L.num_words(n, 4), dtype=torch.int32, device=dev)
+    os_ = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
+    timed("reduce_requant 8x32Mi", f"8 x {n} peers, b4 B128 -> b4 B128 nearest",
+          9 * (oc.numel() * 4 + os_.numel() * 2),
+          lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_))
+    del pc, ps, oc, os_
+
+    # weight difference on an 840 Mi bfloat16 shard, b4 B64
+    n = 840 << 20
+    w_prev = (torch.randn(n, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    w_new = (w_prev.float() + torch.randn(n, device=dev, generator=gen) * 1e-4).to(torch.bfloat16)
+    c = torch.empty(L.num_words(n, 4), dtype=torch.int32, device=dev)
+    s = torch.empty(L.num_blocks(n, 64), dtype=torch.float16, device=dev)
+    w_out = torch.empty_like(w_prev)
+    wb = n * 4 + c.numel() * 4 + s.numel() * 2
+    timed("wdiff_compress 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
+          lambda: L.wdiff_compress(w_new, w_prev, 4, 64, codes=c, scales=s))
+    timed("wdiff_apply 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
+          lambda: L.wdiff_apply(w_prev, c, s, 4, 64, out=w_out))
+    del w_prev, w_new, c, s, w_out
     torch.cuda.synchronize()
     return out
 
