@@ -147,8 +147,7 @@ lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scale
  * multiplied by 2^-floor(L/2), L = log2 B; the result is compressed as by
  * lowbit_quantize_pack (same wire format, same rounding options).  The local
  * reduce is linear and works on such codes unchanged.
- *   n must be a multiple of block_size (EINVAL otherwise); block_size above
- *   2048 returns EUNSUPPORTED.
+ *   n must be a multiple of block_size (EINVAL otherwise).
  */
 lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
                                             const lowbit_qparams* p, uint32_t* codes,

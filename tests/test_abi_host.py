@@ -143,14 +143,12 @@ def test_zero_length_is_a_noop():
 def test_hadamard_size_rules():
     L = lb.lib()
     r = ctypes.byref(_qp(block_size=128))
-    # partial blocks are rejected; blocks above 2048 are not supported
+    # partial blocks are rejected
     assert L.lowbit_hadamard_quantize_pack(None, 0, 200, r, None, None, None) == lb.EINVAL
     assert L.lowbit_hadamard_unpack_dequant(None, None, 200, r, None, None) == lb.EINVAL
     big = ctypes.byref(_qp(block_size=4096))
-    assert L.lowbit_hadamard_quantize_pack(None, 0, 8192, big, None, None,
-                                           None) == lb.EUNSUPPORTED
-    assert L.lowbit_hadamard_unpack_dequant(None, None, 8192, big, None,
-                                            None) == lb.EUNSUPPORTED
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 4096 + 32, big, None, None,
+                                           None) == lb.EINVAL
     # whole blocks of a supported size reach the pointer checks
     assert L.lowbit_hadamard_quantize_pack(None, 0, 256, r, None, None, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, 0, None) == lb.OK

@@ -173,7 +173,7 @@ def test_reduce_unsupported_pairs_raise():
 
 
 # ------------------------------------------------- Hadamard smoothing ----
-HS_BLOCKS = [32, 64, 128, 256, 512, 1024, 2048]
+HS_BLOCKS = [32, 64, 128, 256, 512, 1024, 2048, 4096]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -203,4 +203,4 @@ def test_hadamard_size_rules_raise():
     with pytest.raises(L.LowbitError):
         L.hadamard_quantize_pack(x, 4, 128)
     with pytest.raises(L.LowbitError):
-        L.hadamard_quantize_pack(torch.zeros(8192, device="cuda"), 4, 4096)
+        L.hadamard_quantize_pack(torch.zeros(4096 + 128, device="cuda"), 4, 4096)

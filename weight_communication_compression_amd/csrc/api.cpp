@@ -131,15 +131,13 @@ lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scale
   return launch_dequant(p->bitwidth, false, LOWBIT_F32, a, stream);
 }
 
-// Hadamard smoothing: whole blocks only; blocks up to 2048 elements (the
-// decompress transform runs within one 2048-element trip).
+// Hadamard smoothing: whole blocks only.
 lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
                                             const lowbit_qparams* p, uint32_t* codes,
                                             uint16_t* scales, hipStream_t stream) {
   const int lb = check_params(p);
   if (lb < 0 || n < 0 || n > kMaxN || !valid_dtype(xt)) return LOWBIT_EINVAL;
   if (n % p->block_size != 0) return LOWBIT_EINVAL;
-  if (p->block_size > 2048) return LOWBIT_EUNSUPPORTED;
   if (n == 0) return LOWBIT_OK;
   if (!x || !codes || !scales) return LOWBIT_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;
@@ -156,7 +154,6 @@ lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16
   const int lb = check_params(p);
   if (lb < 0 || n < 0 || n > kMaxN) return LOWBIT_EINVAL;
   if (n % p->block_size != 0) return LOWBIT_EINVAL;
-  if (p->block_size > 2048) return LOWBIT_EUNSUPPORTED;
   if (n == 0) return LOWBIT_OK;
   if (!codes || !scales || !y) return LOWBIT_EINVAL;
   if (!aligned(y, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;

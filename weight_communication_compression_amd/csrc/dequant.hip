@@ -34,7 +34,8 @@ lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a,
 template <int BITS, int LOG2B>
 static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
-  const int64_t ntrips = (nrows + kHadamardRows - 1) / kHadamardRows;
+  constexpr int ROWS = hadamard_rows_per_trip<LOG2B>();
+  const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
   hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>),
                      dim3(grid_for_tiles<kDeqThreads>(ntrips)), dim3(kDeqThreads), 0, s, a);
   return launch_status();
@@ -50,6 +51,7 @@ static lowbit_status launch_hd_b(const DequantArgs& a, hipStream_t s) {
     case 9: return launch_hd<BITS, 9>(a, s);
     case 10: return launch_hd<BITS, 10>(a, s);
     case 11: return launch_hd<BITS, 11>(a, s);
+    case 12: return launch_hd<BITS, 12>(a, s);
   }
   return LOWBIT_EUNSUPPORTED;
 }

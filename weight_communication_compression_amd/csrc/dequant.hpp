@@ -149,18 +149,20 @@ __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
 }
 
 // Decompress followed by the inverse blockwise Walsh-Hadamard transform
-// (blocks of B = 2^LOG2B <= 2048 elements; n is a multiple of B).  Same
-// element-centric layout; a trip of 8 rows (2048 elements) holds whole
-// blocks, so the transform runs in registers: elements within the lane,
-// then lanes, then rows.  Loads and stores are guarded, the transform is
+// (blocks of B = 2^LOG2B elements; n is a multiple of B).  Same element-
+// centric layout (rows of 256, 4 elements per lane); a trip of
+// max(8, B/256) rows holds whole blocks, so the transform runs in registers:
+// elements within the lane, then lanes, then rows.  Loads and stores are guarded, the transform is
 // not (every lane of the wave takes part in the exchanges; lanes past the
 // end hold zeros of blocks that are not stored).
-constexpr int kHadamardRows = 8;
+template <int LOG2B>
+constexpr int hadamard_rows_per_trip() { return (1 << LOG2B) > 8 * kDeqRow ? (1 << LOG2B) / kDeqRow : 8; }
 
 template <int BITS, int LOG2B>
 __global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
   constexpr int E = Grid<BITS>::E;
   constexpr int B = 1 << LOG2B;
+  constexpr int kHadamardRows = hadamard_rows_per_trip<LOG2B>();
   static_assert(B <= kHadamardRows * kDeqRow, "a block must fit in one trip");
   constexpr int LANES = B >= kDeqRow ? kWave : B / 4;
   constexpr int ROWS_PER_BLOCK = B >= kDeqRow ? B / kDeqRow : 1;

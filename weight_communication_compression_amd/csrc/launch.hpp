@@ -62,7 +62,7 @@ lowbit_status launch_reduce_same_ef(int bits, int log2b, bool sr, const ReduceAr
 lowbit_status launch_reduce_mixed(int in_bits, int bits, int log2b, bool sr, bool ef,
                                   const ReduceArgs& a, hipStream_t s);
 lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a, hipStream_t s);
-// decompress + inverse Hadamard, blocks of 32 .. 2048
+// decompress + inverse Hadamard, blocks of 32 .. 4096
 lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_t s);
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
 

@@ -189,7 +189,7 @@ def hadamard_quantize_pack(x: torch.Tensor, bitwidth: int, block_size: int,
                            codes: Optional[torch.Tensor] = None,
                            scales: Optional[torch.Tensor] = None):
     """Blockwise Walsh-Hadamard transform of x, then compress; x.numel() must
-    be a multiple of block_size (<= 2048)."""
+    be a multiple of block_size."""
     n = x.numel()
     codes = _out_codes(n, bitwidth, x, codes)
     scales = _out_scales(n, block_size, x, scales)
