@@ -272,14 +272,16 @@ __device__ __forceinline__ BlockScale make_scale(float t) {
 }
 
 // ----------------------------------------------------------------- hash --
-// MurmurHash3 32-bit finaliser.
-__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
-  h ^= h >> 16;
+// MurmurHash3 32-bit finaliser, and its steps after the first xor-shift.
+__device__ __forceinline__ uint32_t fmix32_after_first_step(uint32_t h) {
   h *= 0x85EBCA6Bu;
   h ^= h >> 13;
   h *= 0xC2B2AE35u;
   h ^= h >> 16;
   return h;
+}
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  return fmix32_after_first_step(h ^ (h >> 16));
 }
 
 // ---------------------------------------------------------------- loads --

@@ -128,18 +128,22 @@ __device__ __forceinline__ void quantize_tile(
       }
     } else {
       word = G::PACK_BIAS;
-      uint32_t hk = 0, lo = 0;
+      // SR: h_j = fmix32((lo + j) ^ hk) for the word's elements j < E.  lo
+      // (the low half of the first element's global index) is a multiple of
+      // E, so lo + j = lo ^ j, and j < 2^16 leaves x >> 16 unchanged: the
+      // first fmix32 step, x ^ (x >> 16), is c ^ j with c computed once.
+      uint32_t c = 0;
       if constexpr (SR) {
         const uint64_t gi = o.index_offset + (uint64_t)i0;
-        hk = fmix32((uint32_t)(gi >> 32) ^ o.key);
-        lo = (uint32_t)gi;
+        const uint32_t x0 = (uint32_t)gi ^ fmix32((uint32_t)(gi >> 32) ^ o.key);
+        c = x0 ^ (x0 >> 16);
       }
 #pragma unroll
       for (int j = 0; j < E; ++j) {
         const float x = v[r][j] * inv;
         float q;
         if constexpr (SR) {
-          const uint32_t h = fmix32((lo + (uint32_t)j) ^ hk);
+          const uint32_t h = fmix32_after_first_step(c ^ (uint32_t)j);
           // the random offset (h >> 8) * 2^-24 is exact, so the fused form
           // rounds once, exactly like adding it in binary32.
           const float y = __builtin_fmaf((float)(h >> 8), 0x1p-24f, x);
