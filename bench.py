@@ -34,8 +34,13 @@ B512 peers to 4-bit B128).  `roundtrip_4mib` times the 2^20-element
 compress + decompress once and over a ring of 256 distinct buffers, issued
 eagerly and from a HIP graph (launch-bound at this size).  `configs` times
 the kernels of the other workload configurations at full size: EF compress of
-128 Mi bfloat16 gradients, the 8 x 32 Mi local reduce, and weight-difference
-compress / apply of an 840 Mi bfloat16 shard.
+128 Mi bfloat16 gradients, the 8 x 32 Mi local reduce (without and with the
+binary32 sum written, each also as a fraction of a reference kernel that only
+reads the peers' streams with the reduce's access pattern), and weight-difference compress / apply of an 840 Mi
+bfloat16 shard.  `size_sweep` gives the latency of one 4-bit compress over
+2^10..2^28 elements beside the CPU oracle's, as a latency curve.  Every
+per-kernel entry also reports `input_GBps`, the full-precision bytes the
+stage handles as stored per second.
 """
 from __future__ import annotations
 
@@ -111,6 +116,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--next-rows", type=int, default=1,
                     help="also time the extension kernels and the 4 MiB roundtrip alone "
+                         "(1) or not (0)")
+    ap.add_argument("--sweep", type=int, default=1,
+                    help="with --next-rows 1, also time the 2^10..2^28 compress latency curve "
                          "(1) or not (0)")
     ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="elements of the bucket the CPU oracle processes (0 = skip)")
@@ -253,9 +261,12 @@ def main() -> int:
     value = full_precision_bytes / (ms_per_step * 1e-3) / 1e9
 
     # plain-copy reference on the same box (not part of the step): the copy
-    # kernel's rate, and its hardware byte counters when profiled
+    # kernel's rate, each launch after a 1 GiB read that leaves the Infinity
+    # Cache clean, and its hardware byte counters when profiled
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     copy_evs = []
     for _ in range(5):
+        flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         run((lib.lowbit_copy_f32, (P(x.data_ptr()), P(y.data_ptr()), N, sh)))
@@ -264,6 +275,7 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_ms = sorted(e0.elapsed_time(e1) for e0, e1 in copy_evs)[2]
     copy_gbs = 2 * N * 4 / (copy_ms * 1e-3) / 1e9
+    del flush
 
     name, kname, alg_bytes, _ = stages[dom]
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
@@ -273,20 +285,40 @@ def main() -> int:
                 "traffic": traffic, "kernel": kname, "stage": name,
                 "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes,
                 "copy_kernel_GBps": round(copy_gbs, 1)}
+    # full-precision bytes each stage handles, as stored: the fp32 bucket (the
+    # 8 peers' fp32-equivalent share for the reduce), the two bf16 weight
+    # tensors read by the weight-difference compress, the bf16 weights read by
+    # the apply
+    def input_bytes(stage):
+        if stage.startswith("reduce_requant"):
+            return PEERS * share * 4
+        if stage.startswith("wdiff_compress"):
+            return 2 * N * 2
+        if stage.startswith("wdiff_apply"):
+            return N * 2
+        return N * 4
+
     kernels = {s[0]: {"us": round(per_stage[i] * 1e3, 2),
                       "alg_GBps": round(s[2] / (per_stage[i] * 1e-3) / 1e9, 1),
-                      "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+                      "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                      "input_GBps": round(input_bytes(s[0]) / (per_stage[i] * 1e-3) / 1e9, 1)}
                for i, s in enumerate(stages)}
 
     # ----------------------------------------- extensions beyond the step --
     next_rows = measure_next_rows(L, lib, dev, stream, x) if args.next_rows else None
     roundtrip = measure_roundtrip(L, dev) if args.next_rows else None
     configs = measure_configs(L, dev) if args.next_rows else None
+    sweep = measure_size_sweep(L, dev, args.cpu_sample > 0) if args.next_rows and args.sweep \
+        else None
 
     # ------------------------------------------------------- CPU oracle --
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(x_host, w_prev_h, w_new_h, min(args.cpu_sample, N), len(stages))
+        threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
+        if threads > 1:
+            cpu["all_cores"] = cpu_baseline_all_cores(x_host, w_prev_h, w_new_h,
+                                                      min(args.cpu_sample, N), len(stages), threads)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -311,6 +343,8 @@ def main() -> int:
         out["roundtrip_4mib"] = roundtrip
     if configs is not None:
         out["configs"] = configs
+    if sweep is not None:
+        out["size_sweep"] = sweep
     print(json.dumps(out), flush=True)
     return 0
 
@@ -428,7 +462,7 @@ def measure_configs(L, dev, reps=20):
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     out = {}
 
-    def timed(name, workload, alg_bytes, fn):
+    def timed(name, workload, alg_bytes, fn, input_bytes):
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -443,7 +477,8 @@ def measure_configs(L, dev, reps=20):
         ms = sorted(ts)[len(ts) // 2]
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
-                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3)}
+                     "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3),
+                     "input_GBps": round(input_bytes / (ms * 1e-3) / 1e9, 1)}
 
     # error feedback on 128 Mi bfloat16 gradients, b4 B128 SR
     n = 128 << 20
@@ -453,7 +488,7 @@ def measure_configs(L, dev, reps=20):
     s = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
     timed("ef_compress 128Mi bf16", f"{n} bf16 N(0,1e-4), fp32 residual, b4 B128 SR",
           n * (2 + 4 + 4) + c.numel() * 4 + s.numel() * 2,
-          lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s))
+          lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s), n * 2)
     del g, e, c, s
 
     # local reduce of 8 peer chunks of 32 Mi, b4 B128 in and out
@@ -469,8 +504,22 @@ def measure_configs(L, dev, reps=20):
     os_ = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
     timed("reduce_requant 8x32Mi", f"8 x {n} peers, b4 B128 -> b4 B128 nearest",
           9 * (oc.numel() * 4 + os_.numel() * 2),
-          lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_))
-    del pc, ps, oc, os_
+          lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_), 8 * n * 4)
+    tot = torch.empty(n, dtype=torch.float32, device=dev)
+    timed("reduce_requant 8x32Mi +sum", f"8 x {n} peers, b4 B128 -> b4 B128 nearest, "
+          "fp32 sum written", 9 * (oc.numel() * 4 + os_.numel() * 2) + n * 4,
+          lambda: L.reduce_requant(pc, ps, n, 4, 128, want_sum=True, out_codes=oc,
+                                   out_scales=os_, out_sum=tot), 8 * n * 4)
+    # bandwidth reference for that access pattern: XOR of the 8 peers' code
+    # streams read the way the reduce reads them, one output stream, no
+    # arithmetic
+    timed("xor_streams 8x16MiB reference", f"XOR of the 8 peers' code streams "
+          f"({oc.numel()} words each) with the reduce's access pattern; not a codec step",
+          9 * oc.numel() * 4, lambda: L.xor_streams(pc, oc), 8 * n * 4)
+    ref = out["xor_streams 8x16MiB reference"]["alg_GBps"]
+    for k in ("reduce_requant 8x32Mi", "reduce_requant 8x32Mi +sum"):
+        out[k]["of_pattern_reference"] = round(out[k]["alg_GBps"] / ref, 3)
+    del pc, ps, oc, os_, tot
 
     # weight difference on an 840 Mi bfloat16 shard, b4 B64
     n = 840 << 20
@@ -481,9 +530,9 @@ def measure_configs(L, dev, reps=20):
     w_out = torch.empty_like(w_prev)
     wb = n * 4 + c.numel() * 4 + s.numel() * 2
     timed("wdiff_compress 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
-          lambda: L.wdiff_compress(w_new, w_prev, 4, 64, codes=c, scales=s))
+          lambda: L.wdiff_compress(w_new, w_prev, 4, 64, codes=c, scales=s), n * 4)
     timed("wdiff_apply 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
-          lambda: L.wdiff_apply(w_prev, c, s, 4, 64, out=w_out))
+          lambda: L.wdiff_apply(w_prev, c, s, 4, 64, out=w_out), n * 2)
     del w_prev, w_new, c, s, w_out
     torch.cuda.synchronize()
     return out
@@ -555,6 +604,127 @@ def measure_roundtrip(L, dev, reps=20, ring=256):
             "ring_eager_GBps": round(total / (eager * 1e-3) / 1e9, 1),
             "ring_graph_GBps": round(total / (replay * 1e-3) / 1e9, 1),
             "ring_graph_frac": round(total / (replay * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+
+
+def measure_size_sweep(L, dev, cpu: bool, reps=20, lo=10, hi=28, cpu_hi=23, burst=20):
+    """Latency of one compress (b4 B128 nearest, fp32 N(0,1)) over sizes
+    2^lo..2^hi, as in the 4-bit quantize latency curve (2^10..2^23 elements,
+    CPU path against GPU path) of the bitscom README, 'Quantization CPU vs GPU
+    Curve'.  Per size: `call_us`, the caller's wall time of one call through
+    the binding plus a synchronize (median of `reps`); `kernel_us`, the GPU
+    time per launch of `burst` launches replayed from a HIP graph (warm: the
+    same buffers each time; below about 2^20 elements this is the dispatch
+    floor, not the kernel); and, up to 2^cpu_hi, the CPU oracle's wall time
+    (one thread, median of 3).  Not part of `value`."""
+    import torch
+
+    bits, block = 4, 128
+    gen = torch.Generator(device=dev).manual_seed(0)
+    side = torch.cuda.Stream(device=dev)
+    rows = []
+    for p in range(lo, hi + 1):
+        n = 1 << p
+        x = torch.randn(n, device=dev, generator=gen)
+        codes = torch.empty(L.num_words(n, bits), dtype=torch.int32, device=dev)
+        scales = torch.empty(L.num_blocks(n, block), dtype=torch.float16, device=dev)
+        alg = n * 4 + codes.numel() * 4 + scales.numel() * 2
+        for _ in range(3):
+            L.quantize_pack(x, bits, block, codes=codes, scales=scales)
+        torch.cuda.synchronize()
+        wall = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            L.quantize_pack(x, bits, block, codes=codes, scales=scales)
+            torch.cuda.synchronize()
+            wall.append(time.perf_counter() - t0)
+        graph = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(burst):
+                    L.quantize_pack(x, bits, block, codes=codes, scales=scales)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        kern = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            kern.append(e0.elapsed_time(e1) * 1e-3 / burst)
+        k, w = sorted(kern)[2], sorted(wall)[reps // 2]
+        row = {"log2_n": p, "kernel_us": round(k * 1e6, 2), "call_us": round(w * 1e6, 2),
+               "alg_GBps": round(alg / k / 1e9, 1)}
+        if cpu and p <= cpu_hi:
+            import oracle as O
+            xh = x.cpu().numpy()
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                O.quantize_pack(xh, bits, block)
+                ts.append(time.perf_counter() - t0)
+            row["cpu_oracle_us"] = round(sorted(ts)[1] * 1e6, 1)
+            row["cpu_over_call"] = round(sorted(ts)[1] / w, 1)
+        rows.append(row)
+        del graph, x, codes, scales
+    return {"workload": f"fp32 N(0,1), b4 B{block} nearest compress, 2^{lo}..2^{hi} elements",
+            "rows": rows}
+
+
+def _block_ranges(n, align, parts):
+    """Split [0, n) into at most `parts` contiguous ranges whose starts are
+    multiples of `align`."""
+    step = -(-max(1, -(-n // parts)) // align) * align
+    return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+
+
+def cpu_baseline_all_cores(x, w_prev, w_new, n, nstages, threads):
+    """The same oracle calls as `cpu_baseline`, split over `threads` host
+    threads by block-aligned element ranges (blocks are independent and the
+    SR hash is keyed on the global index, so the outputs are the same bytes);
+    the C oracle runs without the interpreter lock."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle as O
+
+    xs = np.ascontiguousarray(x[:n])
+    wp, wn = np.ascontiguousarray(w_prev[:n]), np.ascontiguousarray(w_new[:n])
+    share = n // PEERS
+    align = 32 * BLOCK
+    ex = cf.ThreadPoolExecutor(threads)
+
+    def par(fn, total):
+        return list(ex.map(lambda r: fn(*r), _block_ranges(total, align, threads)))
+
+    t0 = time.perf_counter()
+    for b in BITS:
+        parts = par(lambda lo, hi: O.quantize_pack(xs[lo:hi], b, BLOCK, True, SEED, lo), n)
+        c = np.concatenate([p[0] for p in parts])
+        s = np.concatenate([p[1] for p in parts])
+        snw, snb = O.num_words(share, b), O.num_blocks(share, BLOCK)
+
+        def red(lo, hi, b=b, c=c, s=s, snw=snw, snb=snb):
+            w0, w1 = lo * b // 32, O.num_words(hi, b)
+            return O.reduce_requant([c[p * snw + w0:p * snw + w1] for p in range(PEERS)],
+                                    [s[p * snb + lo // BLOCK:p * snb + O.num_blocks(hi, BLOCK)]
+                                     for p in range(PEERS)], hi - lo, b, BLOCK, b)
+        par(red, share)
+        par(lambda lo, hi, b=b, c=c, s=s: O.unpack_dequant(
+            c[lo * b // 32:O.num_words(hi, b)], s[lo // BLOCK:O.num_blocks(hi, BLOCK)],
+            hi - lo, b, BLOCK), n)
+    par(lambda lo, hi: O.ef_compress(xs[lo:hi], np.zeros(hi - lo, np.float32), EF_BITS, BLOCK,
+                                     True, SEED, lo), n)
+
+    def wd(lo, hi):
+        c, s = O.wdiff_compress(wn[lo:hi], wp[lo:hi], W_BITS, W_BLOCK)
+        O.wdiff_apply(wp[lo:hi], c, s, W_BITS, W_BLOCK)
+    par(wd, n)
+    dt = time.perf_counter() - t0
+    ex.shutdown()
+    return {"value": round(nstages * n * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "seconds": round(dt, 2)}
 
 
 def cpu_baseline(x, w_prev, w_new, n, nstages):

@@ -255,6 +255,21 @@ lowbit_status lowbit_wdiff_apply(const void* w_old, const uint32_t* codes, const
  */
 lowbit_status lowbit_copy_f32(const float* x, float* y, int64_t n, hipStream_t stream);
 
+/*
+ * Measurement aid, not a step of the method: out[w] = XOR over the nstreams
+ * streams of streams[p][w], for nwords 32-bit words.  It reads its inputs with
+ * the local reduce's access pattern (every stream at the same offsets, one
+ * 4-byte word per lane) and does none of its arithmetic, so its rate is what
+ * HBM delivers for that pattern: the practical ceiling of the reduce.
+ *   streams : host array of nstreams device pointers (1 <= nstreams <= 16),
+ *             each 4-byte aligned and nwords words long.
+ *   out     : device, nwords words; must not alias a stream.
+ * Errors: EINVAL for nstreams outside [1, 16], nwords < 0, or a null or
+ * misaligned pointer when nwords > 0; nwords == 0 is a no-op.
+ */
+lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nstreams,
+                                     int64_t nwords, uint32_t* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

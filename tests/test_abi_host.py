@@ -109,6 +109,21 @@ def test_null_pointers_and_negative_sizes():
     assert L.lowbit_ef_compress(None, 1, None, 100, r, None, None, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, 10, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, -10, None) == lb.EINVAL
+    streams = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    sp = ctypes.cast(streams, ctypes.c_void_p)
+    for ns in (0, -1, 17):
+        assert L.lowbit_xor_streams_u32(sp, ns, 10, ctypes.c_void_p(0x3000), None) == lb.EINVAL
+    assert L.lowbit_xor_streams_u32(sp, 2, -1, ctypes.c_void_p(0x3000), None) == lb.EINVAL
+    assert L.lowbit_xor_streams_u32(None, 2, 10, ctypes.c_void_p(0x3000), None) == lb.EINVAL
+    assert L.lowbit_xor_streams_u32(sp, 2, 10, None, None) == lb.EINVAL
+    assert L.lowbit_xor_streams_u32(sp, 2, 10, ctypes.c_void_p(0x3002), None) == lb.EINVAL
+    bad = (ctypes.c_void_p * 2)(0x1000, 0x2001)
+    assert L.lowbit_xor_streams_u32(ctypes.cast(bad, ctypes.c_void_p), 2, 10,
+                                    ctypes.c_void_p(0x3000), None) == lb.EINVAL
+    nul = (ctypes.c_void_p * 2)(0x1000, None)
+    assert L.lowbit_xor_streams_u32(ctypes.cast(nul, ctypes.c_void_p), 2, 10,
+                                    ctypes.c_void_p(0x3000), None) == lb.EINVAL
+    assert L.lowbit_xor_streams_u32(None, 1, 0, None, None) == lb.OK
 
 
 def test_misaligned_pointers_rejected():

@@ -269,3 +269,18 @@ def test_copy_kernel():
         L.copy_f32(x, y)
         torch.cuda.synchronize()
         assert torch.equal(x, y)
+
+
+def test_xor_streams_reference_kernel():
+    """The reduce-pattern bandwidth reference: out = XOR of the streams, for
+    stream counts across the group of eight and sizes with a ragged wave."""
+    for P, n in [(1, 1), (3, 127), (8, 128 * 1000), (9, 128 * 3 + 77), (16, (1 << 20) + 5)]:
+        rng = np.random.default_rng(P * 1000 + n)
+        hs = [rng.integers(0, 2 ** 32, n, dtype=np.uint32) for _ in range(P)]
+        gs = [torch.from_numpy(h.view(np.int32)).cuda() for h in hs]
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+        say(f"xor_streams P={P} n={n}")
+        L.xor_streams(gs, out)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(np.stack(hs), axis=0)
+        assert_same(codes_np(out), want, f"xor P={P} n={n}")

@@ -11,7 +11,7 @@ from .lowbit import (  # noqa: F401
     LowbitError, QParams, copy_f32, ef21_compress, ef_compress, hadamard_quantize_pack,
     hadamard_unpack_dequant, lib, library_path, num_blocks,
     num_words, quantize_pack, reduce_requant, reduce_requant_ef, unpack_dequant, wdiff_apply,
-    wdiff_compress,
+    wdiff_compress, xor_streams,
 )
 
 __version__ = "0.1.0"

@@ -312,4 +312,20 @@ lowbit_status lowbit_copy_f32(const float* x, float* y, int64_t n, hipStream_t s
   return launch_copy(x, y, n, stream);
 }
 
+lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nstreams,
+                                     int64_t nwords, uint32_t* out, hipStream_t stream) {
+  if (nstreams < 1 || nstreams > kMaxPeers || nwords < 0 || nwords > kMaxN) return LOWBIT_EINVAL;
+  if (nwords == 0) return LOWBIT_OK;
+  if (!streams || !out || !aligned(out, 4)) return LOWBIT_EINVAL;
+  XorArgs a{};
+  for (int p = 0; p < nstreams; ++p) {
+    if (!streams[p] || !aligned(streams[p], 4)) return LOWBIT_EINVAL;
+    a.streams[p] = streams[p];
+  }
+  a.out = out;
+  a.nwords = nwords;
+  a.nstreams = nstreams;
+  return launch_xor_streams(a, stream);
+}
+
 }  // extern "C"

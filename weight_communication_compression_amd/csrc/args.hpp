@@ -45,4 +45,12 @@ struct DequantArgs {
   void* w_out;             // apply: output weights (may equal w_old)
 };
 
+// Reference kernel with the reduce's access pattern (measurement aid).
+struct XorArgs {
+  const uint32_t* streams[kMaxPeers];
+  uint32_t* out;
+  int64_t nwords;
+  int32_t nstreams;
+};
+
 }  // namespace lowbit

@@ -1,4 +1,5 @@
-// local reduce + requantize kernels: peers and output of the same width
+// local reduce + requantize kernels: peers and output of the same width; the
+// reduce-pattern bandwidth reference
 #include "reduce_tu.hpp"
 
 namespace lowbit {
@@ -12,6 +13,48 @@ lowbit_status launch_reduce_same(int bits, int log2b, bool sr, const ReduceArgs&
     case 8: return launch_r_b<8, 8, false>(log2b, sr, a, s);
   }
   return LOWBIT_EUNSUPPORTED;
+}
+
+// Measurement aid, not a step of the method: out[w] = XOR over the streams
+// of word w.  It has the same-width reduce's access pattern at 4 bits
+// (each wave takes 128 consecutive words of every stream, one 4-byte word per
+// lane in each of two 64-word rows, the loads of up to eight streams in flight
+// before any is combined, one output word per row) and none of its arithmetic,
+// so it shows what HBM delivers for that pattern.
+__global__ __launch_bounds__(kBlockThreads) void xor_streams_kernel(XorArgs a) {
+  constexpr int W = 2, G = 8;
+  const int64_t base = global_wave_id() * (W * kWave);     // wave-uniform
+  if (base >= a.nwords) return;
+  const bool full = base + W * kWave <= a.nwords;
+  const uint32_t lane = (uint32_t)lane_id();
+  uint32_t acc[W] = {0u, 0u};
+#pragma unroll 1
+  for (int g = 0; g < a.nstreams; g += G) {
+    uint32_t v[G][W];
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const uint32_t off = (uint32_t)i * kWave + lane;
+        v[q][i] = (g + q < a.nstreams && (full || base + off < a.nwords))
+                      ? (a.streams[g + q] + base)[off] : 0u;
+      }
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int i = 0; i < W; ++i) acc[i] ^= v[q][i];
+  }
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t off = (uint32_t)i * kWave + lane;
+    if (full || base + off < a.nwords) store_stream(a.out + base + off, acc[i]);
+  }
+}
+
+lowbit_status launch_xor_streams(const XorArgs& a, hipStream_t s) {
+  const int64_t waves = (a.nwords + 2 * kWave - 1) / (2 * kWave);
+  hipLaunchKernelGGL(xor_streams_kernel, dim3(grid_for_tiles(waves)), dim3(kBlockThreads), 0, s, a);
+  return launch_status();
 }
 
 }  // namespace lowbit

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LowbitError", "lib", "library_path", "num_words", "num_blocks", "QParams",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
-    "wdiff_compress", "wdiff_apply", "copy_f32",
+    "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams",
     "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16",
 ]
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "lowbit_wdiff_compress": (ctypes.c_int, [P, P, ctypes.c_int, i64, QP, P, P, P]),
             "lowbit_wdiff_apply": (ctypes.c_int, [P, P, P, i64, QP, P, ctypes.c_int, P]),
             "lowbit_copy_f32": (ctypes.c_int, [P, P, i64, P]),
+            "lowbit_xor_streams_u32": (ctypes.c_int, [P, i32, i64, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -361,3 +362,18 @@ def copy_f32(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
     _check(lib().lowbit_copy_f32(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream(x)),
            "lowbit_copy_f32")
     return y
+
+
+def xor_streams(streams: Sequence[torch.Tensor], out: torch.Tensor) -> torch.Tensor:
+    """out = XOR of the int32 streams, read with the local reduce's access
+    pattern (bandwidth reference for the reduce, not a codec step)."""
+    P = len(streams)
+    n = out.numel()
+    if out.dtype != torch.int32 or any(t.dtype != torch.int32 or t.numel() != n for t in streams):
+        raise LowbitError(EINVAL, "xor_streams needs int32 tensors of equal size")
+    if not 1 <= P <= 16:
+        raise LowbitError(EINVAL, "xor_streams needs 1 to 16 streams")
+    sp = (ctypes.c_void_p * P)(*[_dev(t, "stream") for t in streams])
+    _check(lib().lowbit_xor_streams_u32(ctypes.cast(sp, ctypes.c_void_p), P, n, _dev(out, "out"),
+                                        _stream(out)), "lowbit_xor_streams_u32")
+    return out
