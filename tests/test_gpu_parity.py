@@ -162,6 +162,29 @@ def test_wdiff_compress_apply(bits, B, dtype):
     assert_same(got, want, "apply in place")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rem", range(8))
+def test_wdiff_apply_tail_lanes(rem, dtype):
+    """8-bit apply: a lane covers 8 elements in two code words; with n % 8 in
+    1..4 the tail lane's second word lies past the last code word and is not
+    read."""
+    bits, B = 8, 32
+    n = 512 * 3 + 8 * 5 + rem
+    g = np.random.default_rng(rem)
+    w_old = (g.standard_normal(n) * 0.02).astype(np.float32)
+    w_new = (w_old + g.standard_normal(n) * 1e-3).astype(np.float32)
+    if dtype == "bf16":
+        w_old, w_new = bf16_bits_of(w_old), bf16_bits_of(w_new)
+    wc, ws = O.wdiff_compress(w_new, w_old, bits, B)
+    c = torch.from_numpy(wc.view(np.int32)).cuda()
+    s = torch.from_numpy(ws.view(np.float16)).cuda()
+    say(f"wdiff apply tail bits={bits} {dtype} n={n}")
+    out = L.wdiff_apply(to_gpu(w_old), c, s, bits, B)
+    torch.cuda.synchronize()
+    got = bf16_np(out) if dtype == "bf16" else f32_np(out)
+    assert_same(got, O.wdiff_apply(w_old, wc, ws, bits, B), "apply")
+
+
 # ------------------------------------------------------------- edge cases --
 def test_zero_length_calls_launch_nothing():
     x = torch.empty(0, device="cuda")

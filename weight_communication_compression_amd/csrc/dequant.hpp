@@ -99,8 +99,11 @@ __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
       s16[r] = 0;
       if (r0 + lo < n) {
         const uint32_t* cw = a.codes + r0 / E;
+        // word k holds elements lo + k*E ..: a tail lane of several words
+        // reads only those that hold an element below n
 #pragma unroll
-        for (int k = 0; k < NW; ++k) word[r][k] = cw[lo / E + k];
+        for (int k = 0; k < NW; ++k)
+          if (k == 0 || r0 + lo + (uint32_t)(k * E) < n) word[r][k] = cw[lo / E + k];
         // blocks of >= ROW elements cover the whole row: one scale per row
         s16[r] = a.log2b >= LOG2ROW ? a.scales[r0 >> a.log2b]
                                     : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
