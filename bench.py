@@ -23,8 +23,11 @@ the step time.  Inputs are resident in HBM before the timed region.
 The `roofline` object covers the kernel with the largest share of the step,
 timed with HIP events on the stream the kernels run on; `traffic` comes from
 the committed rocprofv3 counter summary when it was taken on the current
-kernel sources.  `cpu_baseline` times the CPU oracle on a bounded sample of
-the same workload.
+kernel sources.  `roofline.copy_kernel_GBps` is a plain copy's rate and
+`roofline.pattern` times the dominant kernel alone next to a reference
+kernel with its memory pattern and none of its arithmetic (for the EF
+compress: y += x in place over the bucket).  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 
 `next_rows` (not part of `value`) times the extension kernels alone on
 their own workloads: EF21 compress and Hadamard-smoothed compress /
@@ -275,16 +278,45 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_ms = sorted(e0.elapsed_time(e1) for e0, e1 in copy_evs)[2]
     copy_gbs = 2 * N * 4 / (copy_ms * 1e-3) / 1e9
+
+    # the dominant kernel's memory pattern without its arithmetic, and the
+    # kernel itself, each alone after the same flush: for the EF compress the
+    # reference is y += x in place over the bucket (two binary32 streams read,
+    # one rewritten); for any other dominant stage only the kernel is timed
+    def alone(fn, reps=11):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    name, kname, alg_bytes, dom_fa = stages[dom]
+    dom_alone_ms = alone(lambda: run(dom_fa))
+    pattern = {"dominant_alone_us": round(dom_alone_ms * 1e3, 2),
+               "dominant_alone_GBps": round(alg_bytes / (dom_alone_ms * 1e-3) / 1e9, 1)}
+    if name.startswith("ef_compress"):
+        ref_y = torch.zeros_like(x)
+        ref_ms = alone(lambda: run((lib.lowbit_add_inplace_f32,
+                                    (P(x.data_ptr()), P(ref_y.data_ptr()), N, sh))))
+        ref_gbs = 3 * N * 4 / (ref_ms * 1e-3) / 1e9
+        pattern.update({"reference": "y += x in place, 64 Mi binary32 (add_inplace_kernel)",
+                        "reference_GBps": round(ref_gbs, 1),
+                        "of_reference": round(pattern["dominant_alone_GBps"] / ref_gbs, 3)})
+        del ref_y
     del flush
 
-    name, kname, alg_bytes, _ = stages[dom]
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(kname)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname, "stage": name,
                 "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes,
-                "copy_kernel_GBps": round(copy_gbs, 1)}
+                "copy_kernel_GBps": round(copy_gbs, 1), "pattern": pattern}
     # full-precision bytes each stage handles, as stored: the fp32 bucket (the
     # 8 peers' fp32-equivalent share for the reduce), the two bf16 weight
     # tensors read by the weight-difference compress, the bf16 weights read by

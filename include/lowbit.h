@@ -256,6 +256,19 @@ lowbit_status lowbit_wdiff_apply(const void* w_old, const uint32_t* codes, const
 lowbit_status lowbit_copy_f32(const float* x, float* y, int64_t n, hipStream_t stream);
 
 /*
+ * Measurement aid, not a step of the method: y[i] = fl(y[i] + x[i]) in place
+ * for n binary32 values, with the error-feedback compress's access pattern
+ * (two streams read, the second rewritten in place, the same per-wave trip)
+ * and none of its arithmetic or code writes: the practical ceiling of the
+ * error-feedback compress.
+ *   x, y : device, n binary32 values each, 16-byte aligned; y is read and
+ *          overwritten; x must not overlap y.
+ * Errors: EINVAL for n < 0 or a null or misaligned pointer when n > 0;
+ * n == 0 is a no-op.
+ */
+lowbit_status lowbit_add_inplace_f32(const float* x, float* y, int64_t n, hipStream_t stream);
+
+/*
  * Measurement aid, not a step of the method: out[w] = XOR over the nstreams
  * streams of streams[p][w], for nwords 32-bit words.  It reads its inputs with
  * the local reduce's access pattern (every stream at the same offsets, one

@@ -124,6 +124,11 @@ def test_null_pointers_and_negative_sizes():
     assert L.lowbit_xor_streams_u32(ctypes.cast(nul, ctypes.c_void_p), 2, 10,
                                     ctypes.c_void_p(0x3000), None) == lb.EINVAL
     assert L.lowbit_xor_streams_u32(None, 1, 0, None, None) == lb.OK
+    assert L.lowbit_add_inplace_f32(None, None, 10, None) == lb.EINVAL
+    assert L.lowbit_add_inplace_f32(None, None, -1, None) == lb.EINVAL
+    assert L.lowbit_add_inplace_f32(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2008), 10,
+                                    None) == lb.EINVAL
+    assert L.lowbit_add_inplace_f32(None, None, 0, None) == lb.OK
 
 
 def test_misaligned_pointers_rejected():

@@ -10,7 +10,8 @@ import torch
 
 import oracle as O
 from gpu_util import (assert_close_scaled, assert_same, bf16_bits_of, bf16_np, codes_np,
-                      f32_np, mixed_input, say, scale_per_element, scales_np, to_gpu)
+                      f32_np, f32_to_gpu, mixed_input, say, scale_per_element, scales_np,
+                      to_gpu)
 from weight_communication_compression_amd import lowbit as L
 
 pytestmark = pytest.mark.gpu
@@ -307,3 +308,17 @@ def test_xor_streams_reference_kernel():
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(np.stack(hs), axis=0)
         assert_same(codes_np(out), want, f"xor P={P} n={n}")
+
+
+def test_add_inplace_reference_kernel():
+    """The EF-pattern bandwidth reference: y += x in binary32, in place, at
+    sizes with a ragged last wave."""
+    for n in [1, 7, 512, 512 * 3 + 100, (1 << 20) + 13]:
+        rng = np.random.default_rng(n)
+        xh = rng.standard_normal(n).astype(np.float32)
+        yh = rng.standard_normal(n).astype(np.float32)
+        x, y = f32_to_gpu(xh), f32_to_gpu(yh)
+        say(f"add_inplace n={n}")
+        L.add_inplace_f32(x, y)
+        torch.cuda.synchronize()
+        assert_same(f32_np(y), yh + xh, f"add n={n}")

@@ -8,10 +8,10 @@ kernels behind the C ABI of ``liblowbit.so`` (declared in ``include/lowbit.h``);
 input recipes.
 """
 from .lowbit import (  # noqa: F401
-    LowbitError, QParams, copy_f32, ef21_compress, ef_compress, hadamard_quantize_pack,
-    hadamard_unpack_dequant, lib, library_path, num_blocks,
-    num_words, quantize_pack, reduce_requant, reduce_requant_ef, unpack_dequant, wdiff_apply,
-    wdiff_compress, xor_streams,
+    LowbitError, QParams, add_inplace_f32, copy_f32, ef21_compress, ef_compress,
+    hadamard_quantize_pack, hadamard_unpack_dequant, lib, library_path, num_blocks, num_words,
+    quantize_pack, reduce_requant, reduce_requant_ef, unpack_dequant, wdiff_apply, wdiff_compress,
+    xor_streams,
 )
 
 __version__ = "0.1.0"

@@ -312,6 +312,13 @@ lowbit_status lowbit_copy_f32(const float* x, float* y, int64_t n, hipStream_t s
   return launch_copy(x, y, n, stream);
 }
 
+lowbit_status lowbit_add_inplace_f32(const float* x, float* y, int64_t n, hipStream_t stream) {
+  if (n < 0 || n > kMaxN) return LOWBIT_EINVAL;
+  if (n == 0) return LOWBIT_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return LOWBIT_EINVAL;
+  return launch_add_inplace(x, y, n, stream);
+}
+
 lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nstreams,
                                      int64_t nwords, uint32_t* out, hipStream_t stream) {
   if (nstreams < 1 || nstreams > kMaxPeers || nwords < 0 || nwords > kMaxN) return LOWBIT_EINVAL;

@@ -1,4 +1,4 @@
-// decompress, weight-difference apply and the measurement copy kernel
+// decompress, weight-difference apply and the measurement copy and add kernels
 #include "launch.hpp"
 #include "dequant.hpp"
 
@@ -74,6 +74,13 @@ lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, x, y, n);
+  return launch_status();
+}
+
+lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t waves = (n + 8 * kWave - 1) / (8 * kWave);
+  hipLaunchKernelGGL(add_inplace_kernel, dim3(grid_for_tiles(waves)), dim3(kBlockThreads), 0, s,
+                     x, y, n);
   return launch_status();
 }
 

@@ -231,4 +231,31 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, flo
   if (t < n) y[t] = x[t];
 }
 
+// Measurement aid with the error-feedback compress's memory pattern and none
+// of its arithmetic: y[i] = fl(y[i] + x[i]) in place for binary32 x and y, each
+// wave taking 512 consecutive elements (8 per lane: two 16-byte loads of each
+// stream, two 16-byte streaming stores of y), the same trip as the 4-bit EF
+// compress without its code and scale writes.
+__global__ __launch_bounds__(kBlockThreads) void add_inplace_kernel(const float* x, float* y,
+                                                                    int64_t n) {
+  constexpr int E = 8, CHUNK = kWave * E;
+  const int64_t t0 = global_wave_id() * CHUNK;              // wave-uniform
+  if (t0 >= n) return;
+  const uint32_t off = (uint32_t)lane_id() * E;
+  float a[E], b[E];
+  if (t0 + CHUNK <= n) {
+    load_vec<kF32, E>(x, t0, off, a);
+    load_vec<kF32, E>(y, t0, off, b);
+#pragma unroll
+    for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
+    store_vec_f32<E>(y, t0, off, b);
+  } else {
+    load_tail<kF32, E>(x, t0, off, n - t0, a);
+    load_tail<kF32, E>(y, t0, off, n - t0, b);
+#pragma unroll
+    for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
+    store_tail_f32<E>(y, t0, off, n - t0, b);
+  }
+}
+
 }  // namespace lowbit

@@ -65,6 +65,7 @@ lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a,
 // decompress + inverse Hadamard, blocks of 32 .. 4096
 lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_t s);
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
+lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s);
 lowbit_status launch_xor_streams(const XorArgs& a, hipStream_t s);
 
 }  // namespace lowbit

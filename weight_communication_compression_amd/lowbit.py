@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LowbitError", "lib", "library_path", "num_words", "num_blocks", "QParams",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
-    "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams",
+    "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams", "add_inplace_f32",
     "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16",
 ]
 
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "lowbit_wdiff_apply": (ctypes.c_int, [P, P, P, i64, QP, P, ctypes.c_int, P]),
             "lowbit_copy_f32": (ctypes.c_int, [P, P, i64, P]),
             "lowbit_xor_streams_u32": (ctypes.c_int, [P, i32, i64, P, P]),
+            "lowbit_add_inplace_f32": (ctypes.c_int, [P, P, i64, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -361,6 +362,16 @@ def copy_f32(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
         raise LowbitError(EINVAL, "copy_f32 needs two float32 tensors of equal size")
     _check(lib().lowbit_copy_f32(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream(x)),
            "lowbit_copy_f32")
+    return y
+
+
+def add_inplace_f32(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """y += x in place (float32), with the error-feedback compress's access
+    pattern (bandwidth reference for that kernel, not a codec step)."""
+    if x.dtype != torch.float32 or y.dtype != torch.float32 or y.numel() != x.numel():
+        raise LowbitError(EINVAL, "add_inplace_f32 needs two float32 tensors of equal size")
+    _check(lib().lowbit_add_inplace_f32(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream(y)),
+           "lowbit_add_inplace_f32")
     return y
 
 
