@@ -70,6 +70,9 @@ METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HB
 
 # demangled kernel names as rocprofv3 reports them
 def kname_quant(bits, log2b, sr, dt, mode, tail=False):
+    if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
+        return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}>" \
+               f"(lowbit::QuantArgs, long)"
     return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
            f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
 

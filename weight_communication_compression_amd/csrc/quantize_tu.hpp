@@ -5,26 +5,48 @@
 
 #include "launch.hpp"
 #include "quantize.hpp"
+#include "sign.hpp"
 
 namespace lowbit {
 
 // Main kernel over the complete trips of full tiles; one-wave tail kernel for
 // whatever remains (fewer than U full tiles and a partial last tile).
-template <int BITS, int LOG2B, bool SR, int DT, int MODE>
-static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
-  using S = TileShape<BITS, LOG2B>;
-  constexpr int U = compress_tiles_per_trip<S::R * S::E, SR, DT, MODE>();
+// 1-bit compress (every mode but Hadamard smoothing, whose butterflies work
+// on the general tile): one coalesced tile per wave, tail kernel likewise.
+template <int LOG2B, int DT, int MODE>
+static lowbit_status launch_sign(const QuantArgs& a, hipStream_t s) {
+  using S = SignShape<LOG2B>;
   const int64_t full_tiles = a.n / S::TILE;
-  const int64_t ntrips = full_tiles / U;
-  if (ntrips > 0) {
-    hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, false>),
-                       dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+  if (full_tiles > 0) {
+    hipLaunchKernelGGL((sign_kernel<LOG2B, DT, MODE, false>), dim3(grid_for_tiles(full_tiles)),
+                       dim3(kBlockThreads), 0, s, a, full_tiles);
   }
-  if (ntrips * U * S::TILE < a.n) {
-    hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, true>), dim3(1), dim3(kWave),
-                       0, s, a, ntrips * U);
+  if (full_tiles * S::TILE < a.n) {
+    hipLaunchKernelGGL((sign_kernel<LOG2B, DT, MODE, true>), dim3(1), dim3(kWave), 0, s, a,
+                       full_tiles);
   }
   return launch_status();
+}
+
+template <int BITS, int LOG2B, bool SR, int DT, int MODE>
+static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
+  if constexpr (BITS == 1 && MODE != kHadamard) {
+    return launch_sign<LOG2B, DT, MODE>(a, s);
+  } else {
+    using S = TileShape<BITS, LOG2B>;
+    constexpr int U = compress_tiles_per_trip<S::R * S::E, SR, DT, MODE>();
+    const int64_t full_tiles = a.n / S::TILE;
+    const int64_t ntrips = full_tiles / U;
+    if (ntrips > 0) {
+      hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, false>),
+                         dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+    }
+    if (ntrips * U * S::TILE < a.n) {
+      hipLaunchKernelGGL((quantize_kernel<BITS, LOG2B, SR, DT, MODE, true>), dim3(1), dim3(kWave),
+                         0, s, a, ntrips * U);
+    }
+    return launch_status();
+  }
 }
 
 template <int BITS, int LOG2B, int MODE>
