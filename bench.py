@@ -16,6 +16,14 @@ exchange:
   error-feedback compress of the bucket        (b = 4, residual carried over steps)
   weight-difference compress + apply           (64 Mi bfloat16 shard, b = 4, B = 64)
 
+The timed step is issued as a low-bit data-parallel exchange would pipeline
+independent buckets: the error-feedback compress alone on the main stream,
+then the chains {1-bit, 4-bit, weight difference} on the main stream
+concurrently with {2-bit, 8-bit} on a second HIP stream, joined at the
+step's end (each chain keeps its own order; chains write no common buffer).
+`config.ms_per_step_one_stream` gives the same step with every stage on one
+stream, and `kernels` the per-stage durations from that serial form.
+
 `value` counts full-precision (binary32-equivalent) bytes through the step's
 15 stage passes -- each stage touches the 64 Mi elements once -- divided by
 the step time.  Inputs are resident in HBM before the timed region.
@@ -66,6 +74,12 @@ SEED = 42
 PEERS = 8
 W_BITS, W_BLOCK = 4, 64
 EF_BITS = 4
+# How the timed step is issued: the chains run alone on the main stream
+# first, then the chains of the second list on the main stream concurrently
+# with those of the third list on a second stream ("b<bits>": compress ->
+# local reduce -> decompress at that width; "wd": weight-difference compress
+# -> apply; "ef": the error-feedback compress).
+SCHEDULE = (["ef"], ["b1", "b4", "wd"], ["b2", "b8"])
 METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HBM peak"
 
 # demangled kernel names as rocprofv3 reports them
@@ -172,7 +186,7 @@ def main() -> int:
         q = qp(b, BLOCK, True, SEED, 0)
         keep += [codes, scales, q]
         a = (P(x.data_ptr()), L.F32, N, ctypes.byref(q), P(codes.data_ptr()),
-             P(scales.data_ptr()), sh)
+             P(scales.data_ptr()))
         stages.append((f"quantize_pack b{b}", kname_quant(b, 8, b > 1, 0, 0),
                        N * 4 + nw * 4 + nb * 2, (lib.lowbit_quantize_pack, a)))
 
@@ -184,13 +198,14 @@ def main() -> int:
         qi, qo = qp(b, BLOCK), qp(b, BLOCK)
         keep += [cp, spp, rc, rs, qi, qo]
         a = (ctypes.cast(cp, P), ctypes.cast(spp, P), PEERS, share, ctypes.byref(qi),
-             ctypes.byref(qo), P(rc.data_ptr()), P(rs.data_ptr()), None, sh)
+             ctypes.byref(qo), P(rc.data_ptr()), P(rs.data_ptr()), None)
         stages.append((f"reduce_requant b{b}", kname_reduce(b, b, 8, False),
                        (PEERS + 1) * (snw * 4 + snb * 2), (lib.lowbit_reduce_requant, a)))
 
         qd = qp(b, BLOCK)
-        keep.append(qd)
-        a = (P(codes.data_ptr()), P(scales.data_ptr()), N, ctypes.byref(qd), P(y.data_ptr()), sh)
+        yb = torch.empty(N, dtype=torch.float32, device=dev)   # this bitwidth's decompressed bucket
+        keep += [qd, yb]
+        a = (P(codes.data_ptr()), P(scales.data_ptr()), N, ctypes.byref(qd), P(yb.data_ptr()))
         stages.append((f"unpack_dequant b{b}", kname_dequant(b, 0, 0),
                        nw * 4 + nb * 2 + N * 4, (lib.lowbit_unpack_dequant, a)))
 
@@ -200,7 +215,7 @@ def main() -> int:
     qe = qp(EF_BITS, BLOCK, True, SEED, 0)
     keep += [ec, es, qe]
     a = (P(x.data_ptr()), L.F32, P(resid.data_ptr()), N, ctypes.byref(qe), P(ec.data_ptr()),
-         P(es.data_ptr()), sh)
+         P(es.data_ptr()))
     stages.append((f"ef_compress b{EF_BITS}", kname_quant(EF_BITS, 8, True, 0, 1),
                    3 * N * 4 + nw * 4 + nb * 2, (lib.lowbit_ef_compress, a)))
 
@@ -210,30 +225,67 @@ def main() -> int:
     qw = qp(W_BITS, W_BLOCK)
     keep += [wc, ws, qw]
     a = (P(w_new.data_ptr()), P(w_prev.data_ptr()), L.BF16, N, ctypes.byref(qw), P(wc.data_ptr()),
-         P(ws.data_ptr()), sh)
+         P(ws.data_ptr()))
     stages.append((f"wdiff_compress b{W_BITS}", kname_quant(W_BITS, 6, False, 1, 2),
                    2 * N * 2 + nw * 4 + nb * 2, (lib.lowbit_wdiff_compress, a)))
     a = (P(w_prev.data_ptr()), P(wc.data_ptr()), P(ws.data_ptr()), N, ctypes.byref(qw),
-         P(w_out.data_ptr()), L.BF16, sh)
+         P(w_out.data_ptr()), L.BF16)
     stages.append((f"wdiff_apply b{W_BITS}", kname_dequant(W_BITS, 1, 1),
                    2 * N * 2 + nw * 4 + nb * 2, (lib.lowbit_wdiff_apply, a)))
 
     full_precision_bytes = len(stages) * N * 4
 
-    def run(fn_args):
+    def run(fn_args, h=None):
         fn, a = fn_args
-        st = fn(*a)
+        st = fn(*a) if h is None else fn(*a, h)
         if st != 0:
             raise L.LowbitError(st, fn.__name__)
 
     def step(timed_index=None, ev=None):
+        """The stages in order on one stream (events around one stage)."""
         for i, (_, _, _, fa) in enumerate(stages):
             if i == timed_index:
                 ev[0].record(stream)
-                run(fa)
+                run(fa, sh)
                 ev[1].record(stream)
             else:
-                run(fa)
+                run(fa, sh)
+
+    # The step as timed: the EF compress alone on the main stream, then the
+    # independent chains (per bitwidth: compress -> reduce -> decompress; the
+    # weight difference: compress -> apply) split over the main stream and
+    # one more stream, so that one chain's launch ramp, tail and short
+    # latency-bound reduces overlap the other's streaming kernels; joined at
+    # the step's end.  Each chain keeps its own order on its stream, and
+    # chains share no written buffer.
+    side = torch.cuda.Stream(dev)          # default priority
+    side_h = ctypes.c_void_p(side.cuda_stream)
+    fork_ev, join_ev = torch.cuda.Event(), torch.cuda.Event()
+    chain_of = lambda name: "ef" if name.startswith("ef_") else \
+        "wd" if name.startswith("wdiff") else "b" + name.rsplit("b", 1)[1]
+    lanes = [[i for c in SCHEDULE[1] for i, st in enumerate(stages) if chain_of(st[0]) == c],
+             [i for c in SCHEDULE[2] for i, st in enumerate(stages) if chain_of(st[0]) == c]]
+    solo = [i for c in SCHEDULE[0] for i, st in enumerate(stages) if chain_of(st[0]) == c]
+    assert sorted(solo + lanes[0] + lanes[1]) == list(range(len(stages)))
+
+    def step_overlapped(timed_index=None, ev=None):
+        def go(i, h, st):
+            if i == timed_index:
+                ev[0].record(st)
+                run(stages[i][3], h)
+                ev[1].record(st)
+            else:
+                run(stages[i][3], h)
+        for i in solo:
+            go(i, sh, stream)
+        fork_ev.record(stream)
+        side.wait_event(fork_ev)
+        for i in lanes[1]:
+            go(i, side_h, side)
+        for i in lanes[0]:
+            go(i, sh, stream)
+        join_ev.record(side)
+        stream.wait_event(join_ev)
 
     # ------------------------------------------------------------ warmup --
     for _ in range(max(1, args.warmup)):
@@ -253,18 +305,28 @@ def main() -> int:
     dom = max(range(len(stages)), key=lambda i: per_stage[i])
 
     # ------------------------------------------------------------- timed --
+    for _ in range(max(1, args.warmup)):
+        step_overlapped()
     resid.zero_()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(dom, evs[k])
+        step_overlapped(dom, evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
     value = full_precision_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the same step with every stage on one stream, for comparison
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_serial = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # plain-copy reference on the same box (not part of the step): the copy
     # kernel's rate, each launch after a 1 GiB read that leaves the Infinity
@@ -299,7 +361,7 @@ def main() -> int:
         return sorted(ts)[reps // 2]
 
     name, kname, alg_bytes, dom_fa = stages[dom]
-    dom_alone_ms = alone(lambda: run(dom_fa))
+    dom_alone_ms = alone(lambda: run(dom_fa, sh))
     pattern = {"dominant_alone_us": round(dom_alone_ms * 1e3, 2),
                "dominant_alone_GBps": round(alg_bytes / (dom_alone_ms * 1e-3) / 1e9, 1)}
     if name.startswith("ef_compress"):
@@ -319,6 +381,7 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname, "stage": name,
                 "avg_launch_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": alg_bytes,
+                "timed_alone_in_step": dom in solo,
                 "copy_kernel_GBps": round(copy_gbs, 1), "pattern": pattern}
     # full-precision bytes each stage handles, as stored: the fp32 bucket (the
     # 8 peers' fp32-equivalent share for the reduce), the two bf16 weight
@@ -367,6 +430,10 @@ def main() -> int:
                         "compress+apply (64Mi bf16, b4 B64)",
             "elements": N, "block_size": BLOCK, "bitwidths": list(BITS), "peers": PEERS,
             "value_counts": "binary32-equivalent bytes of the 15 stage passes / step time",
+            "schedule": f"{'+'.join(SCHEDULE[0])} alone on the main stream, then "
+                        f"{'+'.join(SCHEDULE[1])} on the main stream concurrently with "
+                        f"{'+'.join(SCHEDULE[2])} on a second stream, joined per step",
+            "ms_per_step_one_stream": round(ms_serial, 4),
             "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
