@@ -178,6 +178,7 @@ def main() -> int:
     P = ctypes.c_void_p
     stages = []      # (name, kernel name, algorithmic bytes, callable)
     keep = []        # keep ctypes objects alive
+    results = {}     # the step's output buffers, checked against the oracle at the end
 
     for b in BITS:
         nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
@@ -205,6 +206,7 @@ def main() -> int:
         qd = qp(b, BLOCK)
         yb = torch.empty(N, dtype=torch.float32, device=dev)   # this bitwidth's decompressed bucket
         keep += [qd, yb]
+        results[f"b{b}"] = (codes, scales, rc, rs, yb)
         a = (P(codes.data_ptr()), P(scales.data_ptr()), N, ctypes.byref(qd), P(yb.data_ptr()))
         stages.append((f"unpack_dequant b{b}", kname_dequant(b, 0, 0),
                        nw * 4 + nb * 2 + N * 4, (lib.lowbit_unpack_dequant, a)))
@@ -224,6 +226,7 @@ def main() -> int:
     ws = torch.empty(nb, dtype=torch.float16, device=dev)
     qw = qp(W_BITS, W_BLOCK)
     keep += [wc, ws, qw]
+    results["wd"] = (wc, ws)
     a = (P(w_new.data_ptr()), P(w_prev.data_ptr()), L.BF16, N, ctypes.byref(qw), P(wc.data_ptr()),
          P(ws.data_ptr()))
     stages.append((f"wdiff_compress b{W_BITS}", kname_quant(W_BITS, 6, False, 1, 2),
@@ -412,7 +415,18 @@ def main() -> int:
     # ------------------------------------------------------- CPU oracle --
     cpu = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(x_host, w_prev_h, w_new_h, min(args.cpu_sample, N), len(stages))
+        cpu, oracle_out = cpu_baseline(x_host, w_prev_h, w_new_h, min(args.cpu_sample, N),
+                                       len(stages))
+        # the step's outputs against the oracle's on the same inputs (the
+        # EF compress once more from a zero residual, as the oracle ran it)
+        n_chk = min(args.cpu_sample, N)
+        e0 = torch.zeros(N, dtype=torch.float32, device=dev)
+        ec0, es0 = L.ef_compress(x, e0, EF_BITS, BLOCK, True, SEED, 0)
+        results["wd"] = results["wd"] + (w_out,)
+        results["ef"] = (ec0, es0, e0)
+        torch.cuda.synchronize()
+        cpu["oracle_check"] = check_against_oracle(results, oracle_out, n_chk, N)
+        del e0, ec0, es0
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
         if threads > 1:
             cpu["all_cores"] = cpu_baseline_all_cores(x_host, w_prev_h, w_new_h,
@@ -831,28 +845,74 @@ def cpu_baseline_all_cores(x, w_prev, w_new, n, nstages, threads):
 
 def cpu_baseline(x, w_prev, w_new, n, nstages):
     """Time the CPU oracle over the first n elements of the same workload
-    (all 15 stage passes), single-threaded; report in the same unit."""
+    (all 15 stage passes), single-threaded; report in the same unit.  Also
+    returns the oracle's outputs (held, not copied, inside the timed region)."""
     import numpy as np
     import oracle as O
 
     xs = np.ascontiguousarray(x[:n])
     wp, wn = np.ascontiguousarray(w_prev[:n]), np.ascontiguousarray(w_new[:n])
     share = n // PEERS
+    outs = {}
     t0 = time.perf_counter()
     for b in BITS:
         c, s = O.quantize_pack(xs, b, BLOCK, True, SEED, 0)
         snw, snb = O.num_words(share, b), O.num_blocks(share, BLOCK)
-        O.reduce_requant([c[p * snw:(p + 1) * snw] for p in range(PEERS)],
-                         [s[p * snb:(p + 1) * snb] for p in range(PEERS)], share, b, BLOCK, b)
-        O.unpack_dequant(c, s, n, b, BLOCK)
-    O.ef_compress(xs, np.zeros(n, np.float32), EF_BITS, BLOCK, True, SEED, 0)
+        rc, rs, _ = O.reduce_requant([c[p * snw:(p + 1) * snw] for p in range(PEERS)],
+                                     [s[p * snb:(p + 1) * snb] for p in range(PEERS)], share, b,
+                                     BLOCK, b)
+        y = O.unpack_dequant(c, s, n, b, BLOCK)
+        outs[f"b{b}"] = (c, s, rc, rs, y)
+    outs["ef"] = O.ef_compress(xs, np.zeros(n, np.float32), EF_BITS, BLOCK, True, SEED, 0)
     c, s = O.wdiff_compress(wn, wp, W_BITS, W_BLOCK)
-    O.wdiff_apply(wp, c, s, W_BITS, W_BLOCK)
+    outs["wd"] = (c, s, O.wdiff_apply(wp, c, s, W_BITS, W_BLOCK))
     dt = time.perf_counter() - t0
     return {"value": round(nstages * n * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {n} elements of the bucket (and of the weight shard), all "
-                      f"{nstages} stage passes, scalar C oracle, one thread"}
+                      f"{nstages} stage passes, scalar C oracle, one thread"}, outs
+
+
+def check_against_oracle(gpu, cpu, n, N):
+    """Bit comparison of the step's GPU outputs with the oracle's on the
+    first n elements (whole blocks); the local reduce only when the oracle ran
+    the full bucket, whose 8 slices are the peers."""
+    import numpy as np
+
+    def bits(t, m):
+        a = t.cpu().numpy()
+        return a.view({4: np.uint32, 2: np.uint16}[a.dtype.itemsize])[:m]
+
+    def raw(a):
+        return a.view({4: np.uint32, 2: np.uint16}[a.dtype.itemsize])
+
+    checked, bad = [], []
+
+    def cmp(name, g, c):
+        c = raw(np.asarray(c))
+        (checked if np.array_equal(bits(g, c.size), c) else bad).append(name)
+
+    for b in BITS:
+        gc, gs, grc, grs, gy = gpu[f"b{b}"]
+        cc, cs, crc, crs, cy = cpu[f"b{b}"]
+        cmp(f"quantize_pack b{b} codes", gc, cc)
+        cmp(f"quantize_pack b{b} scales", gs, cs)
+        if n == N:
+            cmp(f"reduce_requant b{b} codes", grc, crc)
+            cmp(f"reduce_requant b{b} scales", grs, crs)
+        cmp(f"unpack_dequant b{b}", gy, cy)
+    for i, what in enumerate(("codes", "scales", "residual")):
+        cmp(f"ef_compress b{EF_BITS} {what}", gpu["ef"][i], cpu["ef"][i])
+    for i, what in enumerate(("codes", "scales")):
+        cmp(f"wdiff_compress b{W_BITS} {what}", gpu["wd"][i], cpu["wd"][i])
+    cmp(f"wdiff_apply b{W_BITS}", gpu["wd"][2].view(torch_int16()), cpu["wd"][2])
+    return {"elements": n, "outputs_bit_identical": len(bad) == 0, "checked": len(checked) +
+            len(bad), "mismatched": bad}
+
+
+def torch_int16():
+    import torch
+    return torch.int16
 
 
 if __name__ == "__main__":
