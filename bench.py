@@ -409,6 +409,7 @@ def main() -> int:
     next_rows = measure_next_rows(L, lib, dev, stream, x) if args.next_rows else None
     roundtrip = measure_roundtrip(L, dev) if args.next_rows else None
     configs = measure_configs(L, dev) if args.next_rows else None
+    compress_pattern = measure_compress_pattern(L, dev, x) if args.next_rows else None
     sweep = measure_size_sweep(L, dev, args.cpu_sample > 0) if args.next_rows and args.sweep \
         else None
 
@@ -459,6 +460,8 @@ def main() -> int:
         out["roundtrip_4mib"] = roundtrip
     if configs is not None:
         out["configs"] = configs
+    if compress_pattern is not None:
+        out["compress_pattern"] = compress_pattern
     if sweep is not None:
         out["size_sweep"] = sweep
     print(json.dumps(out), flush=True)
@@ -564,6 +567,49 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
            ctypes.byref(qo), P(oc.data_ptr()), P(os_.data_ptr()), None, sh),
           kname_reduce(8, 4, 7, False))
     torch.cuda.synchronize()
+    return out
+
+
+def measure_compress_pattern(L, dev, x, reps=20):
+    """Each compress of the step alone on the bucket beside the reference
+    kernel with its memory volume and none of its arithmetic (reads the
+    binary32 bucket, writes the same number of code words; the scales' 2/B
+    bytes per element are not written): median of `reps`, every launch after
+    a 1 GiB read that leaves the Infinity Cache clean."""
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    N = x.numel()
+
+    def alone(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    out = {}
+    for b in BITS:
+        nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
+        c = torch.empty(nw, dtype=torch.int32, device=dev)
+        s = torch.empty(nb, dtype=torch.float16, device=dev)
+        cms = alone(lambda: L.quantize_pack(x, b, BLOCK, b > 1, SEED, 0, c, s))
+        rms = alone(lambda: L.fold_f32(x, b, c))
+        alg, ref = N * 4 + nw * 4 + nb * 2, N * 4 + nw * 4
+        cg, rg = alg / (cms * 1e-3) / 1e9, ref / (rms * 1e-3) / 1e9
+        out[f"b{b}"] = {"workload": f"{N} fp32 bucket, b{b} B{BLOCK}" + (" SR" if b > 1 else ""),
+                        "compress_us": round(cms * 1e3, 2), "compress_GBps": round(cg, 1),
+                        "frac": round(cg / HBM_PEAK_GBS, 3),
+                        "reference_us": round(rms * 1e3, 2), "reference_GBps": round(rg, 1),
+                        "of_reference": round(cg / rg, 3)}
+        del c, s
     return out
 
 

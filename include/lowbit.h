@@ -283,6 +283,26 @@ lowbit_status lowbit_add_inplace_f32(const float* x, float* y, int64_t n, hipStr
 lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nstreams,
                                      int64_t nwords, uint32_t* out, hipStream_t stream);
 
+/*
+ * Measurement aid, not a step of the method: reads n binary32 values and
+ * writes ceil(n*bitwidth/32) 32-bit words -- the byte volume of a compress at
+ * that bitwidth, less its scales (2/B bytes per value) -- with coalesced
+ * 16-byte loads, one store per lane, and no arithmetic beyond XOR: the
+ * practical ceiling of the compress kernels.  Values are taken in groups of
+ * 2048 (8 rows of 256, four consecutive values per lane and row); lane l of
+ * group g writes words (64g + l)*bitwidth + k, k < bitwidth, word k being the
+ * XOR of the bit patterns of the lane's values 4r + j (r the row, j < 4) with
+ * (4r + j) / (32/bitwidth) == k.  Values past n read as 0; words at or past
+ * ceil(n*bitwidth/32) are not written.
+ *   x   : device, n binary32 values, 16-byte aligned.
+ *   out : device, ceil(n*bitwidth/32) words, 16-byte aligned; must not
+ *         overlap x.
+ * Errors: EINVAL for bitwidth outside {1, 2, 4, 8}, n < 0, or a null or
+ * misaligned pointer when n > 0; n == 0 is a no-op.
+ */
+lowbit_status lowbit_fold_f32(const float* x, int64_t n, int32_t bitwidth, uint32_t* out,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

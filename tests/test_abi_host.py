@@ -109,6 +109,15 @@ def test_null_pointers_and_negative_sizes():
     assert L.lowbit_ef_compress(None, 1, None, 100, r, None, None, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, 10, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, -10, None) == lb.EINVAL
+    assert L.lowbit_fold_f32(None, 10, 4, None, None) == lb.EINVAL
+    assert L.lowbit_fold_f32(None, -1, 4, None, None) == lb.EINVAL
+    assert L.lowbit_fold_f32(ctypes.c_void_p(0x1000), 10, 3, ctypes.c_void_p(0x2000), None) \
+        == lb.EINVAL
+    assert L.lowbit_fold_f32(ctypes.c_void_p(0x1008), 10, 4, ctypes.c_void_p(0x2000), None) \
+        == lb.EINVAL
+    assert L.lowbit_fold_f32(ctypes.c_void_p(0x1000), 10, 4, ctypes.c_void_p(0x2004), None) \
+        == lb.EINVAL
+    assert L.lowbit_fold_f32(None, 0, 4, None, None) == lb.OK
     streams = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     sp = ctypes.cast(streams, ctypes.c_void_p)
     for ns in (0, -1, 17):

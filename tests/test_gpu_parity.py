@@ -322,3 +322,26 @@ def test_add_inplace_reference_kernel():
         L.add_inplace_f32(x, y)
         torch.cuda.synchronize()
         assert_same(f32_np(y), yh + xh, f"add n={n}")
+
+
+def _fold_reference(xh, bits):
+    """The compress-volume reference's output, from its documented layout:
+    groups of 2048 values as 8 rows x 64 lanes x 4, each lane's 32 values
+    (row-major) XOR-folded into `bits` words."""
+    n = xh.size
+    pad = (-n) % 2048
+    v = np.concatenate([xh.view(np.uint32), np.zeros(pad, np.uint32)])
+    g = v.reshape(-1, 8, 64, 4).transpose(0, 2, 1, 3).reshape(-1, 64, bits, 32 // bits)
+    return np.bitwise_xor.reduce(g, axis=3).reshape(-1)[:(n * bits + 31) // 32]
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_fold_reference_kernel(bits):
+    """The compress-volume bandwidth reference at sizes with a ragged group."""
+    for n in [1, 5, 2048, 2048 * 3 + 77, (1 << 20) + 13]:
+        xh = np.random.default_rng(n + bits).standard_normal(n).astype(np.float32)
+        x = f32_to_gpu(xh)
+        say(f"fold bits={bits} n={n}")
+        out = L.fold_f32(x, bits)
+        torch.cuda.synchronize()
+        assert_same(codes_np(out), _fold_reference(xh, bits), f"fold bits={bits} n={n}")

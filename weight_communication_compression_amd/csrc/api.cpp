@@ -335,4 +335,13 @@ lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nst
   return launch_xor_streams(a, stream);
 }
 
+lowbit_status lowbit_fold_f32(const float* x, int64_t n, int32_t bitwidth, uint32_t* out,
+                              hipStream_t stream) {
+  if (n < 0 || n > kMaxN) return LOWBIT_EINVAL;
+  if (bitwidth != 1 && bitwidth != 2 && bitwidth != 4 && bitwidth != 8) return LOWBIT_EINVAL;
+  if (n == 0) return LOWBIT_OK;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return LOWBIT_EINVAL;
+  return launch_fold(x, n, bitwidth, out, stream);
+}
+
 }  // extern "C"

@@ -84,4 +84,18 @@ lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_
   return launch_status();
 }
 
+lowbit_status launch_fold(const float* x, int64_t n, int bits, uint32_t* out, hipStream_t s) {
+  const int64_t tiles = (n + 2047) / 2048;
+  const int64_t nwords = (n * bits + 31) / 32;
+  const dim3 grid(grid_for_tiles(tiles)), block(kBlockThreads);
+  switch (bits) {
+    case 1: hipLaunchKernelGGL(fold_kernel<1>, grid, block, 0, s, x, n, out, nwords); break;
+    case 2: hipLaunchKernelGGL(fold_kernel<2>, grid, block, 0, s, x, n, out, nwords); break;
+    case 4: hipLaunchKernelGGL(fold_kernel<4>, grid, block, 0, s, x, n, out, nwords); break;
+    case 8: hipLaunchKernelGGL(fold_kernel<8>, grid, block, 0, s, x, n, out, nwords); break;
+    default: return LOWBIT_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+
 }  // namespace lowbit

@@ -258,4 +258,55 @@ __global__ __launch_bounds__(kBlockThreads) void add_inplace_kernel(const float*
   }
 }
 
+// Measurement aid with the compress kernels' memory volume and none of their
+// arithmetic: reads n binary32 values and writes ceil(n*BITS/32) words.  A
+// wave takes 2048 consecutive values (8 rows of 256, one 16-byte load per lane
+// per row, as the 1-bit compress reads) and lane l writes BITS consecutive
+// words at word (wave*64 + l)*BITS, word k the XOR of the bit patterns of its
+// values 4r + j in [k*32/BITS, (k+1)*32/BITS) (r the row, j the position in
+// the lane's four); values past n read as 0 and words past the end are not
+// written.
+template <int BITS>
+__global__ __launch_bounds__(kBlockThreads) void fold_kernel(const float* x, int64_t n,
+                                                             uint32_t* out, int64_t nwords) {
+  constexpr int ROWS = 8, ROW = kWave * 4, TILE = ROWS * ROW, PER = 32 / BITS;
+  const int64_t ntiles = (n + TILE - 1) / TILE;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int lane = lane_id();
+  for (int64_t tile = global_wave_id(); tile < ntiles; tile += nwaves) {
+    const int64_t t0 = tile * TILE;
+    uint32_t v[ROWS * 4];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const uint32_t off = (uint32_t)(r * ROW + lane * 4);
+      float f[4];
+      if (t0 + TILE <= n) load_vec<kF32, 4>(x, t0, off, f);
+      else load_tail<kF32, 4>(x, t0, off, n - t0, f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * r + j] = __float_as_uint(f[j]);
+    }
+    uint32_t w[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) {
+      w[k] = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) w[k] ^= v[k * PER + i];
+    }
+    const int64_t o = (tile * kWave + lane) * BITS;
+    if (o + BITS <= nwords) {
+      if constexpr (BITS == 1) store_stream(out + o, w[0]);
+      else if constexpr (BITS == 2) store_stream_words<2>(out + o, w);
+      else if constexpr (BITS == 4) store_stream_words<4>(out + o, w);
+      else {
+        store_stream_words<4>(out + o, w);
+        store_stream_words<4>(out + o + 4, w + 4);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k)
+        if (o + k < nwords) out[o + k] = w[k];
+    }
+  }
+}
+
 }  // namespace lowbit

@@ -304,6 +304,26 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 #endif
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Non-temporal loads of the plain compress's binary32 input where a wave's
+// 16-byte loads cover consecutive 16-byte pieces (the 1-bit compress, and
+// the 8-bit one with 4 elements per lane).  Measured on the 64 Mi bucket:
+// alone, 1 bit 50.4 -> 47 us and 8 bits 61.4 -> 59 us; but a later kernel
+// that reads the same input then finds none of it in the Infinity Cache
+// (in the whole-path step the 2-bit compress after the 1-bit chain goes
+// from 50 to 59 us and the step from 0.633 to 0.663 ms), so the default
+// keeps plain loads.  Where a lane's elements span several 16-byte pieces
+// (2 and 4 bits: 64- and 32-byte lane strides) the hint costs up to 50 %
+// and is never applied.
+#ifndef LOWBIT_X_NT_LOADS
+#define LOWBIT_X_NT_LOADS 0
+#endif
+// Non-temporal loads of the peers' code words in the local reduce (off: the
+// 8 x 32 Mi reduce gains 2-4 %, but each decompress after a reduce in the
+// step loses 10 us).
+#ifndef LOWBIT_REDUCE_NT_LOADS
+#define LOWBIT_REDUCE_NT_LOADS 0
+#endif
+
 // Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
 // in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16); NT: non-temporal
 // (binary32 only).

@@ -67,6 +67,7 @@ lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
 lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s);
 lowbit_status launch_xor_streams(const XorArgs& a, hipStream_t s);
+lowbit_status launch_fold(const float* x, int64_t n, int bits, uint32_t* out, hipStream_t s);
 
 }  // namespace lowbit
 

@@ -184,7 +184,9 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
     float w[E];
     if constexpr (FULL) {
       constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
-      load_vec<DT, E, RMW && LOWBIT_EF_NT_LOADS >= 2>(a.x, t0, off, v[r]);
+      constexpr bool NT_X = (RMW && LOWBIT_EF_NT_LOADS >= 2) ||
+                            (MODE == kPlain && DT == kF32 && E == 4 && LOWBIT_X_NT_LOADS);
+      load_vec<DT, E, NT_X>(a.x, t0, off, v[r]);
       if constexpr (RMW) load_vec<kF32, E, LOWBIT_EF_NT_LOADS >= 1>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, t0, off, w);
     } else {

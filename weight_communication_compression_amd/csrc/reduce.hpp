@@ -70,16 +70,20 @@ constexpr int in_words() { return IN_BITS / BITS; }
 
 template <int M>
 __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   if constexpr (M == 1) {
-    w[0] = *p;
+    w[0] = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(p) : *p;
   } else if constexpr (M == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const u32x2* q = reinterpret_cast<const u32x2*>(p);
+    const u32x2 t = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
     w[0] = t.x;
     w[1] = t.y;
   } else {
 #pragma unroll
     for (int k = 0; k < M / 4; ++k) {
-      const uint4 t = reinterpret_cast<const uint4*>(p)[k];
+      const u32x4* q = reinterpret_cast<const u32x4*>(p) + k;
+      const u32x4 t = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
       w[4 * k + 0] = t.x;
       w[4 * k + 1] = t.y;
       w[4 * k + 2] = t.z;

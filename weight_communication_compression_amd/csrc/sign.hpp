@@ -52,7 +52,7 @@ __device__ __forceinline__ void sign_load(const QuantArgs& a, int64_t t0,
     const uint32_t off = (uint32_t)(r * SignShape<LOG2B>::ROW + lane * 4);
     float w[4];
     if constexpr (FULL) {
-      load_vec<DT, 4>(a.x, t0, off, v[r]);
+      load_vec<DT, 4, MODE == kPlain && LOWBIT_X_NT_LOADS>(a.x, t0, off, v[r]);
       if constexpr (MODE == kErrorFeedback || MODE == kEF21) load_vec<kF32, 4>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, 4>(a.x2, t0, off, w);
     } else {

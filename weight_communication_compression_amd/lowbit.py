@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LowbitError", "lib", "library_path", "num_words", "num_blocks", "QParams",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
-    "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams", "add_inplace_f32",
+    "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams", "add_inplace_f32", "fold_f32",
     "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16",
 ]
 
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "lowbit_copy_f32": (ctypes.c_int, [P, P, i64, P]),
             "lowbit_xor_streams_u32": (ctypes.c_int, [P, i32, i64, P, P]),
             "lowbit_add_inplace_f32": (ctypes.c_int, [P, P, i64, P]),
+            "lowbit_fold_f32": (ctypes.c_int, [P, i64, i32, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -387,4 +388,20 @@ def xor_streams(streams: Sequence[torch.Tensor], out: torch.Tensor) -> torch.Ten
     sp = (ctypes.c_void_p * P)(*[_dev(t, "stream") for t in streams])
     _check(lib().lowbit_xor_streams_u32(ctypes.cast(sp, ctypes.c_void_p), P, n, _dev(out, "out"),
                                         _stream(out)), "lowbit_xor_streams_u32")
+    return out
+
+
+def fold_f32(x: torch.Tensor, bitwidth: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compress-volume bandwidth reference (not a codec step): reads the
+    float32 x, writes num_words(x.numel(), bitwidth) int32 words of XOR folds."""
+    if x.dtype != torch.float32:
+        raise LowbitError(EINVAL, "fold_f32 needs a float32 tensor")
+    n = x.numel()
+    nw = num_words(n, bitwidth)
+    if out is None:
+        out = torch.empty(nw, dtype=torch.int32, device=x.device)
+    elif out.dtype != torch.int32 or out.numel() < nw:
+        raise LowbitError(EINVAL, f"out must be int32 with >= {nw} words")
+    _check(lib().lowbit_fold_f32(_dev(x, "x"), n, int(bitwidth), _dev(out, "out"), _stream(x)),
+           "lowbit_fold_f32")
     return out
