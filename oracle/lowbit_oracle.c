@@ -401,7 +401,10 @@ int oracle_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t
  * in that order, each butterfly (a, b) -> (fl(a + b), fl(a - b)).  The
  * forward result is multiplied by 2^-floor(L/2) and the inverse by
  * 2^-ceil(L/2), L = log2 B, so the pair is the identity in exact arithmetic
- * and both scalings are exact.  n must be a multiple of B.
+ * and both scalings are exact.  R27: the pages give the transform for whole
+ * quantization blocks only; a last block of fewer than B elements (n not a
+ * multiple of B) is compressed and decompressed without it, exactly as the
+ * plain compress and decompress treat a partial block.
  */
 static void walsh_hadamard(float* t, int64_t B)
 {
@@ -427,19 +430,21 @@ int oracle_hadamard_quantize_pack(const void* x, int32_t dtype, int64_t n, int32
 {
     int rc = check_q(bits, block, n, index_offset);
     if (rc) return rc;
-    if (n % block != 0) return ORACLE_EINVAL;
     int64_t nw = oracle_num_words(n, bits);
     for (int64_t w = 0; w < nw; ++w) codes[w] = 0;
     float* a = (float*)malloc(sizeof(float) * (size_t)block);
     if (!a) return ORACLE_EINVAL;
     float f = ldexpf(1.0f, -(log2_of(block) / 2));
-    int64_t nb = n / block;
+    int64_t nb = oracle_num_blocks(n, block);
     for (int64_t k = 0; k < nb; ++k) {
         int64_t lo = k * block;
-        for (int64_t j = 0; j < block; ++j) a[j] = load_elem(x, dtype, lo + j);
-        walsh_hadamard(a, block);
-        for (int64_t j = 0; j < block; ++j) a[j] = a[j] * f;
-        scales[k] = quantize_block(a, block, block, bits, bits == 1 ? 0 : stochastic, seed,
+        int64_t nvalid = (n - lo < block) ? (n - lo) : block;
+        for (int64_t j = 0; j < nvalid; ++j) a[j] = load_elem(x, dtype, lo + j);
+        if (nvalid == block) {              /* a partial last block is not transformed */
+            walsh_hadamard(a, block);
+            for (int64_t j = 0; j < block; ++j) a[j] = a[j] * f;
+        }
+        scales[k] = quantize_block(a, nvalid, block, bits, bits == 1 ? 0 : stochastic, seed,
                                    index_offset + (uint64_t)lo, codes, lo, NULL);
     }
     free(a);
@@ -450,26 +455,28 @@ int oracle_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales
                                    int32_t bits, int32_t block, float* y)
 {
     if (!valid_bits(bits) || !valid_block(block) || n < 0) return ORACLE_EINVAL;
-    if (n % block != 0) return ORACLE_EINVAL;
     float f = ldexpf(1.0f, -((log2_of(block) + 1) / 2));
     for (int64_t lo = 0; lo < n; lo += block) {
         float s = oracle_f16_to_f32(scales[lo / block]);
-        for (int64_t j = 0; j < block; ++j)
+        int64_t nvalid = (n - lo < block) ? (n - lo) : block;
+        for (int64_t j = 0; j < nvalid; ++j)
             y[lo + j] = dequant_code(get_code(codes, lo + j, bits), bits, s);
-        walsh_hadamard(y + lo, block);
-        for (int64_t j = 0; j < block; ++j) y[lo + j] = y[lo + j] * f;
+        if (nvalid == block) {              /* a partial last block is not transformed */
+            walsh_hadamard(y + lo, block);
+            for (int64_t j = 0; j < block; ++j) y[lo + j] = y[lo + j] * f;
+        }
     }
     return ORACLE_OK;
 }
 
-/* The transform alone (forward: inverse = 0, inverse: inverse = 1), on whole
- * blocks of x in place. */
+/* The transform alone (forward: inverse = 0, inverse: inverse = 1), on the
+ * whole blocks of x in place (a partial last block is left as it is). */
 int oracle_hadamard_blocks(float* x, int64_t n, int32_t block, int32_t inverse)
 {
-    if (!valid_block(block) || n < 0 || n % block != 0) return ORACLE_EINVAL;
+    if (!valid_block(block) || n < 0) return ORACLE_EINVAL;
     int L = log2_of(block);
     float f = ldexpf(1.0f, inverse ? -((L + 1) / 2) : -(L / 2));
-    for (int64_t lo = 0; lo < n; lo += block) {
+    for (int64_t lo = 0; lo + block <= n; lo += block) {
         walsh_hadamard(x + lo, block);
         for (int64_t j = 0; j < block; ++j) x[lo + j] = x[lo + j] * f;
     }

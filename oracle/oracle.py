@@ -309,7 +309,8 @@ def ef21_compress(g, state, bits: int, block: int, stochastic: bool = False, see
 
 def hadamard_quantize_pack(x, bits: int, block: int, stochastic: bool = False, seed: int = 0,
                            index_offset: int = 0):
-    """Blockwise Hadamard transform, then compress.  Returns (codes, scales)."""
+    """Blockwise Hadamard transform, then compress (a partial last block is
+    compressed untransformed).  Returns (codes, scales)."""
     dt, x = _as_input(x)
     n = x.size
     codes = np.empty(num_words(n, bits), np.uint32)
@@ -321,7 +322,8 @@ def hadamard_quantize_pack(x, bits: int, block: int, stochastic: bool = False, s
 
 
 def hadamard_unpack_dequant(codes, scales, n: int, bits: int, block: int) -> np.ndarray:
-    """Decompress, then the inverse blockwise Hadamard transform."""
+    """Decompress, then the inverse blockwise Hadamard transform (not on a
+    partial last block)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint32)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     y = np.empty(n, np.float32)
@@ -331,7 +333,8 @@ def hadamard_unpack_dequant(codes, scales, n: int, bits: int, block: int) -> np.
 
 
 def hadamard_blocks(x, block: int, inverse: bool = False) -> np.ndarray:
-    """The scaled blockwise transform alone (a copy of x is transformed)."""
+    """The scaled blockwise transform alone on a copy of x (whole blocks; a
+    partial last block is left as it is)."""
     y = np.array(x, dtype=np.float32, copy=True)
     _check(lib().oracle_hadamard_blocks(_ptr(y), y.size, block, int(inverse)), "hadamard_blocks")
     return y

@@ -342,13 +342,39 @@ def test_hadamard_lowers_error_on_heavy_tailed_data(oracle_mod, bits, B):
     assert mse_hs < 0.5 * mse_plain
 
 
-def test_hadamard_rejects_partial_blocks(oracle_mod):
-    x = np.ones(200, np.float32)
-    with pytest.raises(ValueError):
-        oracle_mod.hadamard_quantize_pack(x, 4, 128)
-    with pytest.raises(ValueError):
-        oracle_mod.hadamard_unpack_dequant(np.zeros(25, np.uint32), np.zeros(2, np.uint16), 200,
-                                           4, 128)
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+@pytest.mark.parametrize("B", [32, 128, 4096])
+@pytest.mark.parametrize("rem", [1, 7, 31])
+def test_hadamard_partial_last_block_is_plain(oracle_mod, bits, B, rem):
+    """A last block of rem < B elements is compressed and decompressed without
+    the transform: the whole blocks give what the smoothed codec gives on
+    them alone, and the partial block gives what the pinned plain compress
+    and decompress give on it, at its global index."""
+    k = 3 if B < 4096 else 1
+    n = k * B + rem
+    x = np.random.default_rng(B + rem + bits).standard_t(3, n).astype(np.float32)
+    c, s = oracle_mod.hadamard_quantize_pack(x, bits, B, True, 5, 4 * B)
+    c0, s0 = oracle_mod.hadamard_quantize_pack(x[:k * B], bits, B, True, 5, 4 * B)
+    ct, st = oracle_mod.quantize_pack(x[k * B:], bits, B, True, 5, 4 * B + k * B)
+    w0 = k * B * bits // 32
+    assert np.array_equal(c[:w0], c0) and np.array_equal(s[:k], s0)
+    assert np.array_equal(c[w0:], ct) and np.array_equal(s[k:], st)
+    y = oracle_mod.hadamard_unpack_dequant(c, s, n, bits, B)
+    assert np.array_equal(y[:k * B], oracle_mod.hadamard_unpack_dequant(c0, s0, k * B, bits, B))
+    assert np.array_equal(y[k * B:], oracle_mod.unpack_dequant(ct, st, rem, bits, B))
+    t = oracle_mod.hadamard_blocks(x, B)
+    assert np.array_equal(t[:k * B], oracle_mod.hadamard_blocks(x[:k * B], B))
+    assert np.array_equal(t[k * B:], x[k * B:])
+
+
+def test_hadamard_partial_only_block_is_plain(oracle_mod):
+    """n < B: the single partial block is the plain codec's."""
+    x = np.random.default_rng(3).standard_normal(100).astype(np.float32)
+    c, s = oracle_mod.hadamard_quantize_pack(x, 4, 128)
+    wc, ws = oracle_mod.quantize_pack(x, 4, 128)
+    assert np.array_equal(c, wc) and np.array_equal(s, ws)
+    assert np.array_equal(oracle_mod.hadamard_unpack_dequant(c, s, 100, 4, 128),
+                          oracle_mod.unpack_dequant(wc, ws, 100, 4, 128))
 
 
 def test_hadamard_handworked_stage_order(oracle_mod):
