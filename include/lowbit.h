@@ -146,8 +146,10 @@ lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scale
  * fl(a-b)) of stride 1, 2, ..., B/2 in that order on binary32 values -- and
  * multiplied by 2^-floor(L/2), L = log2 B; the result is compressed as by
  * lowbit_quantize_pack (same wire format, same rounding options).  The local
- * reduce is linear and works on such codes unchanged.
- *   n must be a multiple of block_size (EINVAL otherwise).
+ * reduce is linear and works on such codes unchanged.  When n is not a
+ * multiple of block_size, the last, partial block is compressed without the
+ * transform, exactly as lowbit_quantize_pack compresses it (the pages give
+ * the transform for whole blocks only).
  */
 lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
                                             const lowbit_qparams* p, uint32_t* codes,
@@ -157,7 +159,8 @@ lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int6
  * Decompress with the inverse smoothing: dequantize, apply the same
  * butterflies per block and multiply by 2^-ceil(L/2) (the two scalings
  * multiply to 1/B, so the pair of transforms is the identity in exact
- * arithmetic).  Same size rules as lowbit_hadamard_quantize_pack.
+ * arithmetic).  A partial last block (n not a multiple of block_size) is
+ * decompressed without the inverse transform, as lowbit_unpack_dequant does.
  */
 lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales,
                                              int64_t n, const lowbit_qparams* p, float* y,

@@ -171,15 +171,17 @@ def test_zero_length_is_a_noop():
 
 def test_hadamard_size_rules():
     L = lb.lib()
+    # block sizes outside 32..4096 or not powers of two are rejected
+    for B in (16, 96, 8192):
+        bad = ctypes.byref(_qp(block_size=B))
+        assert L.lowbit_hadamard_quantize_pack(None, 0, 256, bad, None, None, None) == lb.EINVAL
+        assert L.lowbit_hadamard_unpack_dequant(None, None, 256, bad, None, None) == lb.EINVAL
+    # any length, ragged or not, reaches the pointer checks (null -> EINVAL)
+    # and n == 0 is a no-op
     r = ctypes.byref(_qp(block_size=128))
-    # partial blocks are rejected
-    assert L.lowbit_hadamard_quantize_pack(None, 0, 200, r, None, None, None) == lb.EINVAL
-    assert L.lowbit_hadamard_unpack_dequant(None, None, 200, r, None, None) == lb.EINVAL
-    big = ctypes.byref(_qp(block_size=4096))
-    assert L.lowbit_hadamard_quantize_pack(None, 0, 4096 + 32, big, None, None,
-                                           None) == lb.EINVAL
-    # whole blocks of a supported size reach the pointer checks
-    assert L.lowbit_hadamard_quantize_pack(None, 0, 256, r, None, None, None) == lb.EINVAL
+    for n in (200, 256, 4096 + 32):
+        assert L.lowbit_hadamard_quantize_pack(None, 0, n, r, None, None, None) == lb.EINVAL
+    assert L.lowbit_hadamard_quantize_pack(None, 0, 0, r, None, None, None) == lb.OK
     assert L.lowbit_copy_f32(None, None, 0, None) == lb.OK
 
 

@@ -182,7 +182,9 @@ HS_BLOCKS = [32, 64, 128, 256, 512, 1024, 2048, 4096]
 @pytest.mark.parametrize("bits", [1, 2, 4, 8])
 def test_hadamard_compress_decompress(bits, B, sr, dtype):
     T = _tile(bits, B)
-    for i, n in enumerate(sorted({B, 3 * B, 4 * T + B, 9 * T})):
+    # whole blocks, and ragged ends: a partial last block is not transformed
+    for i, n in enumerate(sorted({B, 3 * B, 4 * T + B, 9 * T, 5, B - 1, 3 * B + 1,
+                                  4 * T + B + 37, 9 * T + B - 3})):
         x = mixed_input(3000 + bits * B + i, n) if i % 2 else \
             np.random.default_rng(i).standard_t(3, n).astype(np.float32)
         xin = bf16_bits_of(x) if dtype == "bf16" else x
@@ -200,7 +202,8 @@ def test_hadamard_compress_decompress(bits, B, sr, dtype):
 
 def test_hadamard_size_rules_raise():
     x = torch.zeros(200, device="cuda")
+    for B in (16, 96, 8192):
+        with pytest.raises(L.LowbitError):
+            L.hadamard_quantize_pack(x, 4, B)
     with pytest.raises(L.LowbitError):
-        L.hadamard_quantize_pack(x, 4, 128)
-    with pytest.raises(L.LowbitError):
-        L.hadamard_quantize_pack(torch.zeros(4096 + 128, device="cuda"), 4, 4096)
+        L.hadamard_quantize_pack(x, 3, 128)

@@ -131,13 +131,12 @@ lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scale
   return launch_dequant(p->bitwidth, false, LOWBIT_F32, a, stream);
 }
 
-// Hadamard smoothing: whole blocks only.
+// Hadamard smoothing: whole blocks transformed, a partial last block not.
 lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
                                             const lowbit_qparams* p, uint32_t* codes,
                                             uint16_t* scales, hipStream_t stream) {
   const int lb = check_params(p);
   if (lb < 0 || n < 0 || n > kMaxN || !valid_dtype(xt)) return LOWBIT_EINVAL;
-  if (n % p->block_size != 0) return LOWBIT_EINVAL;
   if (n == 0) return LOWBIT_OK;
   if (!x || !codes || !scales) return LOWBIT_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;
@@ -153,7 +152,6 @@ lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16
                                              hipStream_t stream) {
   const int lb = check_params(p);
   if (lb < 0 || n < 0 || n > kMaxN) return LOWBIT_EINVAL;
-  if (n % p->block_size != 0) return LOWBIT_EINVAL;
   if (n == 0) return LOWBIT_OK;
   if (!codes || !scales || !y) return LOWBIT_EINVAL;
   if (!aligned(y, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return LOWBIT_EINVAL;

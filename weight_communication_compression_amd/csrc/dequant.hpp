@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantAr
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t n = a.n;
   const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
+  const int64_t nfull = n & ~(int64_t)(B - 1);   // elements in whole blocks
   const uint32_t lo = 4u * (uint32_t)lane;
 
   for (int64_t base = wave * kHadamardRows; base < nrows; base += nwaves * kHadamardRows) {
@@ -198,11 +199,21 @@ __global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantAr
     for (int r = 0; r < kHadamardRows; ++r)
       decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
     hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK>(d, hadamard_inverse_scale<LOG2B>());
+    // a partial last block is decompressed untransformed: its lanes decode
+    // their values again (only a trip that reaches past the whole blocks)
+    if ((base + kHadamardRows) * kDeqRow > nfull) {
+#pragma unroll
+      for (int r = 0; r < kHadamardRows; ++r) {
+        const int64_t i = (base + r) * kDeqRow + lo;
+        if (i >= nfull)
+          decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < kHadamardRows; ++r) {
       const int64_t r0 = (base + r) * kDeqRow;
-      // n is a multiple of B >= 32, so a lane's 4 elements are all valid or none
-      if (r0 + lo < n) store_vec_f32<4>(a.y, r0, lo, d[r]);
+      if (r0 + lo + 4 <= n) store_vec_f32<4>(a.y, r0, lo, d[r]);
+      else if (r0 + lo < n) store_tail_f32<4>(a.y, r0, lo, n - r0, d[r]);
     }
   }
 }

@@ -206,8 +206,27 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
     }
   }
   // the tile holds whole blocks: B / E lanes of one row, or all R rows
-  if constexpr (MODE == kHadamard)
-    hadamard_rows<R, E, S::L, R>(v, hadamard_forward_scale<LOG2B>());
+  if constexpr (MODE == kHadamard) {
+    if constexpr (FULL) {
+      hadamard_rows<R, E, S::L, R>(v, hadamard_forward_scale<LOG2B>());
+    } else {
+      // a partial last block is compressed untransformed: every lane takes
+      // part in the exchanges, then that block's lanes take back their loads
+      float v0[R][E];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < E; ++j) v0[r][j] = v[r][j];
+      hadamard_rows<R, E, S::L, R>(v, hadamard_forward_scale<LOG2B>());
+      const int64_t blk0 = (R == 1) ? t0 + (int64_t)(lane / S::L) * S::B : t0;
+      if (blk0 + S::B > a.n) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < E; ++j) v[r][j] = v0[r][j];
+      }
+    }
+  }
 }
 
 // Quantize one loaded tile; in error-feedback mode also write e = a - deq,

@@ -191,8 +191,8 @@ def hadamard_quantize_pack(x: torch.Tensor, bitwidth: int, block_size: int,
                            stochastic: bool = False, seed: int = 0, index_offset: int = 0,
                            codes: Optional[torch.Tensor] = None,
                            scales: Optional[torch.Tensor] = None):
-    """Blockwise Walsh-Hadamard transform of x, then compress; x.numel() must
-    be a multiple of block_size."""
+    """Blockwise Walsh-Hadamard transform of x, then compress; a partial last
+    block (x.numel() not a multiple of block_size) is compressed untransformed."""
     n = x.numel()
     codes = _out_codes(n, bitwidth, x, codes)
     scales = _out_scales(n, block_size, x, scales)
