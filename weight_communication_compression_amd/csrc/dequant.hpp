@@ -157,14 +157,22 @@ __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
 }
 
 // Decompress followed by the inverse blockwise Walsh-Hadamard transform
-// (blocks of B = 2^LOG2B elements; n is a multiple of B).  Same element-
-// centric layout (rows of 256, 4 elements per lane); a trip of
-// max(8, B/256) rows holds whole blocks, so the transform runs in registers:
-// elements within the lane, then lanes, then rows.  Loads and stores are guarded, the transform is
-// not (every lane of the wave takes part in the exchanges; lanes past the
-// end hold zeros of blocks that are not stored).
+// (blocks of B = 2^LOG2B elements).  Same element-centric layout (rows of
+// 256, 4 elements per lane); a trip of max(LOWBIT_HS_DEQ_ROWS, B/256) rows
+// holds whole blocks, so the transform runs in registers: elements within
+// the lane, then lanes, then rows.  Loads and stores are guarded, the
+// transform is not (every lane of the wave takes part in the exchanges;
+// lanes past the end hold values that are not stored).  Rows per trip,
+// measured on the 64 Mi bucket at 4 bits, B = 128: 1 row 83 us, 2: 65,
+// 4: 63, 8: 60.6, 16: 75 (more rows keep more exchanges in flight per wave
+// until the register footprint costs occupancy).
+#ifndef LOWBIT_HS_DEQ_ROWS
+#define LOWBIT_HS_DEQ_ROWS 8
+#endif
 template <int LOG2B>
-constexpr int hadamard_rows_per_trip() { return (1 << LOG2B) > 8 * kDeqRow ? (1 << LOG2B) / kDeqRow : 8; }
+constexpr int hadamard_rows_per_trip() {
+  return (1 << LOG2B) > LOWBIT_HS_DEQ_ROWS * kDeqRow ? (1 << LOG2B) / kDeqRow : LOWBIT_HS_DEQ_ROWS;
+}
 
 template <int BITS, int LOG2B>
 __global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
