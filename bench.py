@@ -924,6 +924,7 @@ def check_against_oracle(gpu, cpu, n, N):
     first n elements (whole blocks); the local reduce only when the oracle ran
     the full bucket, whose 8 slices are the peers."""
     import numpy as np
+    import torch
 
     def bits(t, m):
         a = t.cpu().numpy()
@@ -951,14 +952,9 @@ def check_against_oracle(gpu, cpu, n, N):
         cmp(f"ef_compress b{EF_BITS} {what}", gpu["ef"][i], cpu["ef"][i])
     for i, what in enumerate(("codes", "scales")):
         cmp(f"wdiff_compress b{W_BITS} {what}", gpu["wd"][i], cpu["wd"][i])
-    cmp(f"wdiff_apply b{W_BITS}", gpu["wd"][2].view(torch_int16()), cpu["wd"][2])
+    cmp(f"wdiff_apply b{W_BITS}", gpu["wd"][2].view(torch.int16), cpu["wd"][2])
     return {"elements": n, "outputs_bit_identical": len(bad) == 0, "checked": len(checked) +
             len(bad), "mismatched": bad}
-
-
-def torch_int16():
-    import torch
-    return torch.int16
 
 
 if __name__ == "__main__":
