@@ -87,6 +87,9 @@ def kname_quant(bits, log2b, sr, dt, mode, tail=False):
     if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
         return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}>" \
                f"(lowbit::QuantArgs, long)"
+    if bits in (2, 4) and mode in (1, 3):     # 2- and 4-bit EF / EF21: the row layout
+        return f"void lowbit::row_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
+               f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
     return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
            f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
 

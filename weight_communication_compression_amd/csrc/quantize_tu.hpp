@@ -5,6 +5,7 @@
 
 #include "launch.hpp"
 #include "quantize.hpp"
+#include "rowq.hpp"
 #include "sign.hpp"
 
 namespace lowbit {
@@ -28,10 +29,42 @@ static lowbit_status launch_sign(const QuantArgs& a, hipStream_t s) {
   return launch_status();
 }
 
+// 2- and 4-bit compress in the row layout: the error-feedback and EF21
+// modes (LOWBIT_ROW_LAYOUT_EF), the plain and weight-difference modes
+// (LOWBIT_ROW_LAYOUT_PLAIN); Hadamard smoothing keeps the general tile.
+#ifndef LOWBIT_ROW_LAYOUT_EF
+#define LOWBIT_ROW_LAYOUT_EF 1
+#endif
+#ifndef LOWBIT_ROW_LAYOUT_PLAIN
+#define LOWBIT_ROW_LAYOUT_PLAIN 0
+#endif
+template <int MODE>
+constexpr bool use_row_layout() {
+  return (MODE == kErrorFeedback || MODE == kEF21) ? LOWBIT_ROW_LAYOUT_EF
+         : (MODE == kPlain || MODE == kWeightDiff) ? LOWBIT_ROW_LAYOUT_PLAIN
+                                                   : false;
+}
+template <int BITS, int LOG2B, bool SR, int DT, int MODE>
+static lowbit_status launch_row(const QuantArgs& a, hipStream_t s) {
+  using S = RowShape<BITS, LOG2B, MODE>;
+  const int64_t full_trips = a.n / S::TILE;
+  if (full_trips > 0) {
+    hipLaunchKernelGGL((row_kernel<BITS, LOG2B, SR, DT, MODE, false>),
+                       dim3(grid_for_tiles(full_trips)), dim3(kBlockThreads), 0, s, a, full_trips);
+  }
+  if (full_trips * S::TILE < a.n) {
+    hipLaunchKernelGGL((row_kernel<BITS, LOG2B, SR, DT, MODE, true>), dim3(1), dim3(kWave), 0, s,
+                       a, full_trips);
+  }
+  return launch_status();
+}
+
 template <int BITS, int LOG2B, bool SR, int DT, int MODE>
 static lowbit_status launch_q(const QuantArgs& a, hipStream_t s) {
   if constexpr (BITS == 1 && MODE != kHadamard) {
     return launch_sign<LOG2B, DT, MODE>(a, s);
+  } else if constexpr ((BITS == 2 || BITS == 4) && use_row_layout<MODE>()) {
+    return launch_row<BITS, LOG2B, SR, DT, MODE>(a, s);
   } else {
     using S = TileShape<BITS, LOG2B>;
     constexpr int U = compress_tiles_per_trip<S::R * S::E, SR, DT, MODE>();

@@ -39,17 +39,16 @@ struct SignShape {
   static constexpr int WPL = RT / 8;                     // code words kept per lane
 };
 
-// Load one tile (plus the residual, minus the old weights, or minus the EF21
-// state, as in the general compress); positions at or past n read +0.
-template <int LOG2B, int DT, int MODE, bool FULL>
-__device__ __forceinline__ void sign_load(const QuantArgs& a, int64_t t0,
-                                          float (&v)[SignShape<LOG2B>::RT][4],
-                                          float (&h)[SignShape<LOG2B>::RT][4]) {
-  constexpr int RT = SignShape<LOG2B>::RT;
+// Load RT rows of 256 elements from element t0, four consecutive elements
+// per lane and row (plus the residual, minus the old weights, or minus the
+// EF21 state, as in the general compress); positions at or past n read +0.
+template <int RT, int DT, int MODE, bool FULL>
+__device__ __forceinline__ void row_load(const QuantArgs& a, int64_t t0, float (&v)[RT][4],
+                                         float (&h)[RT][4]) {
   const int lane = lane_id();
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const uint32_t off = (uint32_t)(r * SignShape<LOG2B>::ROW + lane * 4);
+    const uint32_t off = (uint32_t)(r * kWave * 4 + lane * 4);
     float w[4];
     if constexpr (FULL) {
       load_vec<DT, 4, MODE == kPlain && LOWBIT_X_NT_LOADS>(a.x, t0, off, v[r]);
@@ -184,10 +183,10 @@ __global__ __launch_bounds__(kBlockThreads) void sign_kernel(QuantArgs a, int64_
       const int64_t t0 = tile * S::TILE;
       float v[RT][4], h[RT][4];
       if (t0 + S::TILE <= a.n) {
-        sign_load<LOG2B, DT, MODE, true>(a, t0, v, h);
+        row_load<RT, DT, MODE, true>(a, t0, v, h);
         sign_finish<LOG2B, MODE, true>(a, t0, v, h);
       } else {
-        sign_load<LOG2B, DT, MODE, false>(a, t0, v, h);
+        row_load<RT, DT, MODE, false>(a, t0, v, h);
         sign_finish<LOG2B, MODE, false>(a, t0, v, h);
       }
     }
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(kBlockThreads) void sign_kernel(QuantArgs a, int64_
     for (int64_t tile = global_wave_id(); tile < first; tile += nwaves) {
       const int64_t t0 = tile * S::TILE;
       float v[RT][4], h[RT][4];
-      sign_load<LOG2B, DT, MODE, true>(a, t0, v, h);
+      row_load<RT, DT, MODE, true>(a, t0, v, h);
       sign_finish<LOG2B, MODE, true>(a, t0, v, h);
     }
   }
