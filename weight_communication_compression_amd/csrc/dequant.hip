@@ -78,7 +78,7 @@ lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
 }
 
 lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s) {
-  const int64_t waves = (n + 8 * kWave - 1) / (8 * kWave);
+  const int64_t waves = (n + 4 * kWave - 1) / (4 * kWave);
   hipLaunchKernelGGL(add_inplace_kernel, dim3(grid_for_tiles(waves)), dim3(kBlockThreads), 0, s,
                      x, y, n);
   return launch_status();

@@ -252,12 +252,12 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, flo
 
 // Measurement aid with the error-feedback compress's memory pattern and none
 // of its arithmetic: y[i] = fl(y[i] + x[i]) in place for binary32 x and y, each
-// wave taking 512 consecutive elements (8 per lane: two 16-byte loads of each
-// stream, two 16-byte streaming stores of y), the same trip as the 4-bit EF
-// compress without its code and scale writes.
+// wave taking one row of 256 consecutive elements (4 per lane: one 16-byte
+// load of each stream, one 16-byte streaming store of y), the same trip as
+// the 4-bit EF compress's row layout without its code and scale writes.
 __global__ __launch_bounds__(kBlockThreads) void add_inplace_kernel(const float* x, float* y,
                                                                     int64_t n) {
-  constexpr int E = 8, CHUNK = kWave * E;
+  constexpr int E = 4, CHUNK = kWave * E;
   const int64_t t0 = global_wave_id() * CHUNK;              // wave-uniform
   if (t0 >= n) return;
   const uint32_t off = (uint32_t)lane_id() * E;
