@@ -51,8 +51,10 @@ __device__ __forceinline__ void row_load(const QuantArgs& a, int64_t t0, float (
     const uint32_t off = (uint32_t)(r * kWave * 4 + lane * 4);
     float w[4];
     if constexpr (FULL) {
-      load_vec<DT, 4, MODE == kPlain && LOWBIT_X_NT_LOADS>(a.x, t0, off, v[r]);
-      if constexpr (MODE == kErrorFeedback || MODE == kEF21) load_vec<kF32, 4>(a.resid, t0, off, w);
+      constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
+      load_vec<DT, 4, (MODE == kPlain && LOWBIT_X_NT_LOADS) || (RMW && LOWBIT_EF_NT_LOADS >= 2)>(
+          a.x, t0, off, v[r]);
+      if constexpr (RMW) load_vec<kF32, 4, LOWBIT_EF_NT_LOADS >= 1>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, 4>(a.x2, t0, off, w);
     } else {
       load_tail<DT, 4>(a.x, t0, off, a.n - t0, v[r]);
