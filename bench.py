@@ -919,7 +919,22 @@ def cpu_baseline(x, w_prev, w_new, n, nstages):
     return {"value": round(nstages * n * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {n} elements of the bucket (and of the weight shard), all "
-                      f"{nstages} stage passes, scalar C oracle, one thread"}, outs
+                      f"{nstages} stage passes, scalar C oracle, one thread",
+            "host": host_cpu()}, outs
+
+
+def host_cpu():
+    """The host's CPU model and the threads this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "threads_available": len(os.sched_getaffinity(0)),
+            "nproc": os.cpu_count()}
 
 
 def check_against_oracle(gpu, cpu, n, N):
