@@ -66,6 +66,87 @@ __device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* 
   decode_n<BITS, 4>(word, off, s, d);
 }
 
+// One trip of the decompress / apply: rows base .. base + rows - 1.  GUARD:
+// the trip may reach past n (the last one only); the others load and store
+// unguarded.
+template <int BITS, int APPLY, int DT, bool GUARD>
+__device__ __forceinline__ void dequant_trip(const DequantArgs& a, int64_t base) {
+  constexpr int E = Grid<BITS>::E;              // codes per word
+  constexpr int kDequantRows = dequant_rows<APPLY>();
+  constexpr int EPL = dequant_epl<APPLY>();
+  constexpr int ROW = kWave * EPL;
+  constexpr int NW = EPL * BITS > 32 ? EPL * BITS / 32 : 1;   // words per lane
+  constexpr int LOG2ROW = EPL == 8 ? 9 : 8;
+  const int lane = lane_id();
+  const int64_t n = a.n;
+  uint32_t word[kDequantRows][NW];
+  uint32_t s16[kDequantRows];
+  float wo[kDequantRows][EPL];
+  const uint32_t lo = (uint32_t)EPL * (uint32_t)lane;       // lane's element within a row
+#pragma unroll
+  for (int r = 0; r < kDequantRows; ++r) {
+    const int64_t r0 = (base + r) * ROW;                    // row start (wave-uniform)
+#pragma unroll
+    for (int k = 0; k < NW; ++k) word[r][k] = 0;
+    s16[r] = 0;
+    if (!GUARD || r0 + lo < n) {
+      const uint32_t* cw = a.codes + r0 / E;
+      // word k holds elements lo + k*E ..: a tail lane of several words
+      // reads only those that hold an element below n
+#pragma unroll
+      for (int k = 0; k < NW; ++k)
+        if (!GUARD || k == 0 || r0 + lo + (uint32_t)(k * E) < n) word[r][k] = cw[lo / E + k];
+      // blocks of >= ROW elements cover the whole row: one scale per row
+      s16[r] = a.log2b >= LOG2ROW ? a.scales[r0 >> a.log2b]
+                                  : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
+      if constexpr (APPLY) {
+        if (!GUARD || r0 + lo + EPL <= n) load_vec<DT, EPL>(a.w_old, r0, lo, wo[r]);
+        else load_tail<DT, EPL>(a.w_old, r0, lo, n - r0, wo[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kDequantRows; ++r) {
+    const int64_t r0 = (base + r) * ROW;
+    if (GUARD && r0 + lo >= n) continue;
+    float d[EPL];
+    const float s = f16_bits_to_f32(s16[r]);
+    if constexpr (NW == 1) {
+      decode_n<BITS, EPL>(word[r][0], (int)(lo % E) * BITS, s, d);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) decode_n<BITS, E>(word[r][k], 0, s, d + k * E);
+    }
+    const bool full = !GUARD || r0 + lo + EPL <= n;
+    if constexpr (!APPLY) {
+      if (full) store_vec_f32<EPL>(a.y, r0, lo, d);
+      else store_tail_f32<EPL>(a.y, r0, lo, n - r0, d);
+    } else {
+      float w[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) w[j] = wo[r][j] + d[j];
+      if constexpr (DT == kF32) {
+        if (full) store_vec_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, w);
+        else store_tail_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, n - r0, w);
+      } else {
+        const int64_t e0 = r0 + lo;
+        uint16_t* out = static_cast<uint16_t*>(a.w_out) + r0 + lo;
+        if (full) {
+          uint32_t pk[EPL / 2];
+#pragma unroll
+          for (int k = 0; k < EPL / 2; ++k)
+            pk[k] = f32_to_bf16_rne(w[2 * k]) | (f32_to_bf16_rne(w[2 * k + 1]) << 16);
+          store_stream_words<EPL / 2>(reinterpret_cast<uint32_t*>(out), pk);
+        } else {
+#pragma unroll
+          for (int j = 0; j < EPL; ++j)
+            if (e0 + j < n) out[j] = (uint16_t)f32_to_bf16_rne(w[j]);
+        }
+      }
+    }
+  }
+}
+
 // APPLY: 0 = decompress to binary32; 1 = weight-difference apply.  Element-
 // centric: a row is 64 * EPL consecutive elements, lane l decodes elements
 // EPL*l .. EPL*l + EPL - 1 (their codes are EPL*b consecutive bits of one
@@ -73,86 +154,16 @@ __device__ __forceinline__ void decode4(uint32_t word, int off, float s, float* 
 // each lane needs one scale.
 template <int BITS, int APPLY, int DT>
 __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
-  constexpr int E = Grid<BITS>::E;              // codes per word
   constexpr int kDequantRows = dequant_rows<APPLY>();
-  constexpr int EPL = dequant_epl<APPLY>();
-  constexpr int ROW = kWave * EPL;
-  constexpr int NW = EPL * BITS > 32 ? EPL * BITS / 32 : 1;   // words per lane
-  constexpr int LOG2ROW = EPL == 8 ? 9 : 8;
-  static_assert(ROW == 1 << LOG2ROW, "rows of 256 or 512 elements");
-  const int lane = lane_id();
+  constexpr int ROW = kWave * dequant_epl<APPLY>();
+  static_assert(ROW == 256 || ROW == 512, "rows of 256 or 512 elements");
   const int64_t wave = global_wave_id<kDeqThreads>();
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
-  const int64_t n = a.n;
-  const int64_t nrows = (n + ROW - 1) / ROW;
-
+  const int64_t nrows = (a.n + ROW - 1) / ROW;
   for (int64_t base = wave * kDequantRows; base < nrows; base += nwaves * kDequantRows) {
-    uint32_t word[kDequantRows][NW];
-    uint32_t s16[kDequantRows];
-    float wo[kDequantRows][EPL];
-    const uint32_t lo = (uint32_t)EPL * (uint32_t)lane;       // lane's element within a row
-#pragma unroll
-    for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t r0 = (base + r) * ROW;                    // row start (wave-uniform)
-#pragma unroll
-      for (int k = 0; k < NW; ++k) word[r][k] = 0;
-      s16[r] = 0;
-      if (r0 + lo < n) {
-        const uint32_t* cw = a.codes + r0 / E;
-        // word k holds elements lo + k*E ..: a tail lane of several words
-        // reads only those that hold an element below n
-#pragma unroll
-        for (int k = 0; k < NW; ++k)
-          if (k == 0 || r0 + lo + (uint32_t)(k * E) < n) word[r][k] = cw[lo / E + k];
-        // blocks of >= ROW elements cover the whole row: one scale per row
-        s16[r] = a.log2b >= LOG2ROW ? a.scales[r0 >> a.log2b]
-                                    : (a.scales + (r0 >> a.log2b))[lo >> a.log2b];
-        if constexpr (APPLY) {
-          if (r0 + lo + EPL <= n) load_vec<DT, EPL>(a.w_old, r0, lo, wo[r]);
-          else load_tail<DT, EPL>(a.w_old, r0, lo, n - r0, wo[r]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kDequantRows; ++r) {
-      const int64_t r0 = (base + r) * ROW;
-      if (r0 + lo >= n) continue;
-      float d[EPL];
-      const float s = f16_bits_to_f32(s16[r]);
-      if constexpr (NW == 1) {
-        decode_n<BITS, EPL>(word[r][0], (int)(lo % E) * BITS, s, d);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) decode_n<BITS, E>(word[r][k], 0, s, d + k * E);
-      }
-      const bool full = r0 + lo + EPL <= n;
-      if constexpr (!APPLY) {
-        if (full) store_vec_f32<EPL>(a.y, r0, lo, d);
-        else store_tail_f32<EPL>(a.y, r0, lo, n - r0, d);
-      } else {
-        float w[EPL];
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) w[j] = wo[r][j] + d[j];
-        if constexpr (DT == kF32) {
-          if (full) store_vec_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, w);
-          else store_tail_f32<EPL>(static_cast<float*>(a.w_out), r0, lo, n - r0, w);
-        } else {
-          const int64_t e0 = r0 + lo;
-          uint16_t* out = static_cast<uint16_t*>(a.w_out) + r0 + lo;
-          if (full) {
-            uint32_t pk[EPL / 2];
-#pragma unroll
-            for (int k = 0; k < EPL / 2; ++k)
-              pk[k] = f32_to_bf16_rne(w[2 * k]) | (f32_to_bf16_rne(w[2 * k + 1]) << 16);
-            store_stream_words<EPL / 2>(reinterpret_cast<uint32_t*>(out), pk);
-          } else {
-#pragma unroll
-            for (int j = 0; j < EPL; ++j)
-              if (e0 + j < n) out[j] = (uint16_t)f32_to_bf16_rne(w[j]);
-          }
-        }
-      }
-    }
+    // wave-uniform: every trip but the last lies inside the buffer
+    if ((base + kDequantRows) * ROW <= a.n) dequant_trip<BITS, APPLY, DT, false>(a, base);
+    else dequant_trip<BITS, APPLY, DT, true>(a, base);
   }
 }
 
@@ -174,55 +185,64 @@ constexpr int hadamard_rows_per_trip() {
   return (1 << LOG2B) > LOWBIT_HS_DEQ_ROWS * kDeqRow ? (1 << LOG2B) / kDeqRow : LOWBIT_HS_DEQ_ROWS;
 }
 
-template <int BITS, int LOG2B>
-__global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
+// One trip of the decompress with inverse smoothing: rows base ..
+// base + rows - 1.  GUARD: the trip may reach past n (the last one only).
+template <int BITS, int LOG2B, bool GUARD>
+__device__ __forceinline__ void hadamard_dequant_trip(const DequantArgs& a, int64_t base) {
   constexpr int E = Grid<BITS>::E;
   constexpr int B = 1 << LOG2B;
   constexpr int kHadamardRows = hadamard_rows_per_trip<LOG2B>();
-  static_assert(B <= kHadamardRows * kDeqRow, "a block must fit in one trip");
   constexpr int LANES = B >= kDeqRow ? kWave : B / 4;
   constexpr int ROWS_PER_BLOCK = B >= kDeqRow ? B / kDeqRow : 1;
-  const int lane = lane_id();
+  const int64_t n = a.n;
+  const int64_t nfull = n & ~(int64_t)(B - 1);   // elements in whole blocks
+  const uint32_t lo = 4u * (uint32_t)lane_id();
+  uint32_t word[kHadamardRows], s16[kHadamardRows];
+#pragma unroll
+  for (int r = 0; r < kHadamardRows; ++r) {
+    const int64_t r0 = (base + r) * kDeqRow;
+    word[r] = 0;
+    s16[r] = 0;
+    if (!GUARD || r0 + lo < n) {
+      word[r] = (a.codes + r0 / E)[lo / E];
+      s16[r] = LOG2B >= 8 ? a.scales[r0 >> LOG2B] : (a.scales + (r0 >> LOG2B))[lo >> LOG2B];
+    }
+  }
+  float d[kHadamardRows][4];
+#pragma unroll
+  for (int r = 0; r < kHadamardRows; ++r)
+    decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
+  hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK>(d, hadamard_inverse_scale<LOG2B>());
+  // a partial last block is decompressed untransformed: its lanes decode
+  // their values again (only a trip that reaches past the whole blocks)
+  if ((base + kHadamardRows) * kDeqRow > nfull) {
+#pragma unroll
+    for (int r = 0; r < kHadamardRows; ++r) {
+      const int64_t i = (base + r) * kDeqRow + lo;
+      if (i >= nfull)
+        decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kHadamardRows; ++r) {
+    const int64_t r0 = (base + r) * kDeqRow;
+    if (!GUARD || r0 + lo + 4 <= n) store_vec_f32<4>(a.y, r0, lo, d[r]);
+    else if (r0 + lo < n) store_tail_f32<4>(a.y, r0, lo, n - r0, d[r]);
+  }
+}
+
+template <int BITS, int LOG2B>
+__global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
+  constexpr int B = 1 << LOG2B;
+  constexpr int kHadamardRows = hadamard_rows_per_trip<LOG2B>();
+  static_assert(B <= kHadamardRows * kDeqRow, "a block must fit in one trip");
   const int64_t wave = global_wave_id<kDeqThreads>();
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
-  const int64_t n = a.n;
-  const int64_t nrows = (n + kDeqRow - 1) / kDeqRow;
-  const int64_t nfull = n & ~(int64_t)(B - 1);   // elements in whole blocks
-  const uint32_t lo = 4u * (uint32_t)lane;
-
+  const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   for (int64_t base = wave * kHadamardRows; base < nrows; base += nwaves * kHadamardRows) {
-    uint32_t word[kHadamardRows], s16[kHadamardRows];
-#pragma unroll
-    for (int r = 0; r < kHadamardRows; ++r) {
-      const int64_t r0 = (base + r) * kDeqRow;
-      word[r] = 0;
-      s16[r] = 0;
-      if (r0 + lo < n) {
-        word[r] = (a.codes + r0 / E)[lo / E];
-        s16[r] = LOG2B >= 8 ? a.scales[r0 >> LOG2B] : (a.scales + (r0 >> LOG2B))[lo >> LOG2B];
-      }
-    }
-    float d[kHadamardRows][4];
-#pragma unroll
-    for (int r = 0; r < kHadamardRows; ++r)
-      decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
-    hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK>(d, hadamard_inverse_scale<LOG2B>());
-    // a partial last block is decompressed untransformed: its lanes decode
-    // their values again (only a trip that reaches past the whole blocks)
-    if ((base + kHadamardRows) * kDeqRow > nfull) {
-#pragma unroll
-      for (int r = 0; r < kHadamardRows; ++r) {
-        const int64_t i = (base + r) * kDeqRow + lo;
-        if (i >= nfull)
-          decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kHadamardRows; ++r) {
-      const int64_t r0 = (base + r) * kDeqRow;
-      if (r0 + lo + 4 <= n) store_vec_f32<4>(a.y, r0, lo, d[r]);
-      else if (r0 + lo < n) store_tail_f32<4>(a.y, r0, lo, n - r0, d[r]);
-    }
+    // wave-uniform: every trip but the last lies inside the buffer
+    if ((base + kHadamardRows) * kDeqRow <= a.n) hadamard_dequant_trip<BITS, LOG2B, false>(a, base);
+    else hadamard_dequant_trip<BITS, LOG2B, true>(a, base);
   }
 }
 
