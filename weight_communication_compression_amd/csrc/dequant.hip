@@ -35,9 +35,10 @@ template <int BITS, int LOG2B>
 static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   constexpr int ROWS = hadamard_rows_per_trip<LOG2B>();
-  const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
+  // one wave per LOWBIT_HS_DEQ_TRIPS trips
+  const int64_t waves = (nrows + ROWS * LOWBIT_HS_DEQ_TRIPS - 1) / (ROWS * LOWBIT_HS_DEQ_TRIPS);
   hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>),
-                     dim3(grid_for_tiles<kDeqThreads>(ntrips)), dim3(kDeqThreads), 0, s, a);
+                     dim3(grid_for_tiles<kDeqThreads>(waves)), dim3(kDeqThreads), 0, s, a);
   return launch_status();
 }
 
