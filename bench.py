@@ -95,6 +95,9 @@ def kname_quant(bits, log2b, sr, dt, mode, tail=False):
 
 
 def kname_reduce(in_bits, bits, log2b, sr, ef=False, tail=False):
+    if in_bits == bits == 4 and ef:     # 4-bit reduce with a residual: the row layout
+        return f"void lowbit::rowr_kernel<{bits}, {log2b}, {str(sr).lower()}, " \
+               f"{str(ef).lower()}, {str(tail).lower()}>(lowbit::ReduceArgs, long)"
     return f"void lowbit::reduce_kernel<{in_bits}, {bits}, {log2b}, {str(sr).lower()}, " \
            f"{str(ef).lower()}, {str(tail).lower()}>(lowbit::ReduceArgs, long)"
 

@@ -5,26 +5,56 @@
 
 #include "launch.hpp"
 #include "reduce.hpp"
+#include "rowr.hpp"
 
 namespace lowbit {
+
+// 4-bit same-width reduce in the row layout when a binary32 stream is part
+// of it (the stage-2 residual or the sum output): measured on 8 x 32 Mi
+// peers, b4 B128, with residual 83 -> 75 us, with the sum 65 -> 57 us.  The
+// plain reduce keeps the general tile (40 -> 49 us in the row layout, where
+// two lanes load each code word and every lane its scale; at 2 bits
+// 33 -> 58 us).
+#ifndef LOWBIT_ROW_REDUCE_4
+#define LOWBIT_ROW_REDUCE_4 1
+#endif
+template <int BITS, int LOG2B, bool SR, bool EF>
+static lowbit_status launch_rr(const ReduceArgs& a, hipStream_t s) {
+  using S = RowShape<BITS, LOG2B, EF ? kErrorFeedback : kPlain>;
+  const int64_t full_trips = a.n / S::TILE;
+  if (full_trips > 0) {
+    hipLaunchKernelGGL((rowr_kernel<BITS, LOG2B, SR, EF, false>), dim3(grid_for_tiles(full_trips)),
+                       dim3(kBlockThreads), 0, s, a, full_trips);
+  }
+  if (full_trips * S::TILE < a.n) {
+    hipLaunchKernelGGL((rowr_kernel<BITS, LOG2B, SR, EF, true>), dim3(1), dim3(kWave), 0, s, a,
+                       full_trips);
+  }
+  return launch_status();
+}
 
 // Main kernel over the complete trips of full tiles; one-wave tail kernel for
 // whatever remains.
 template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF>
 static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
-  using S = TileShape<BITS, LOG2B>;
-  constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
-  const int64_t full_tiles = a.n / S::TILE;
-  const int64_t ntrips = full_tiles / U;
-  if (ntrips > 0) {
-    hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, false>),
-                       dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+  if constexpr (IN_BITS == BITS && BITS == 4 && LOWBIT_ROW_REDUCE_4) {
+    if (EF || a.out_sum) return launch_rr<BITS, LOG2B, SR, EF>(a, s);
   }
-  if (ntrips * U * S::TILE < a.n) {
-    hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, true>), dim3(1), dim3(kWave),
-                       0, s, a, ntrips * U);
+  {
+    using S = TileShape<BITS, LOG2B>;
+    constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
+    const int64_t full_tiles = a.n / S::TILE;
+    const int64_t ntrips = full_tiles / U;
+    if (ntrips > 0) {
+      hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, false>),
+                         dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
+    }
+    if (ntrips * U * S::TILE < a.n) {
+      hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, true>), dim3(1),
+                         dim3(kWave), 0, s, a, ntrips * U);
+    }
+    return launch_status();
   }
-  return launch_status();
 }
 
 // stochastic rounding does not apply to a 1-bit output
