@@ -83,15 +83,18 @@ SCHEDULE = (["ef"], ["b1", "b4", "wd"], ["b2", "b8"])
 METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HBM peak"
 
 # demangled kernel names as rocprofv3 reports them
-def kname_quant(bits, log2b, sr, dt, mode, tail=False):
+def kname_quant(bits, log2b, sr, dt, mode, tail=False, stream=False):
+    """stream: the non-temporal-input form (plain binary32 compress at 1 and 8
+    bits without LOWBIT_HINT_INPUT_REUSED)."""
+    ntx = str(bool(stream) and mode == 0 and dt == 0 and bits in (1, 8) and not tail).lower()
     if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
-        return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}>" \
+        return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}, {ntx}>" \
                f"(lowbit::QuantArgs, long)"
     if bits in (2, 4) and mode in (1, 3):     # 2- and 4-bit EF / EF21: the row layout
         return f"void lowbit::row_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
                f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
     return f"void lowbit::quantize_kernel<{bits}, {log2b}, {str(sr).lower()}, {dt}, {mode}, " \
-           f"{str(tail).lower()}>(lowbit::QuantArgs, long)"
+           f"{str(tail).lower()}, {ntx}>(lowbit::QuantArgs, long)"
 
 
 def kname_reduce(in_bits, bits, log2b, sr, ef=False, tail=False):
@@ -148,6 +151,9 @@ def main() -> int:
                          "(1) or not (0)")
     ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="elements of the bucket the CPU oracle processes (0 = skip)")
+    ap.add_argument("--cpu-configs", type=int, default=1,
+                    help="with --cpu-sample > 0, also time the CPU oracle on each workload "
+                         "configuration, one thread and all threads (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -178,8 +184,8 @@ def main() -> int:
     y = torch.empty(N, dtype=torch.float32, device=dev)
     w_out = torch.empty_like(w_prev)
 
-    def qp(bits, block, sr=False, seed=0, off=0):
-        return L.QParams(bits, block, int(sr), 0, seed, off)
+    def qp(bits, block, sr=False, seed=0, off=0, hints=0):
+        return L.QParams(bits, block, int(sr), hints, seed, off)
 
     P = ctypes.c_void_p
     stages = []      # (name, kernel name, algorithmic bytes, callable)
@@ -190,7 +196,9 @@ def main() -> int:
         nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
         codes = torch.empty(nw, dtype=torch.int32, device=dev)
         scales = torch.empty(nb, dtype=torch.float16, device=dev)
-        q = qp(b, BLOCK, True, SEED, 0)
+        # the step compresses the bucket again at the next width (and in the
+        # next step), so its compresses keep the input in the caches
+        q = qp(b, BLOCK, True, SEED, 0, L.HINT_INPUT_REUSED)
         keep += [codes, scales, q]
         a = (P(x.data_ptr()), L.F32, N, ctypes.byref(q), P(codes.data_ptr()),
              P(scales.data_ptr()))
@@ -442,6 +450,8 @@ def main() -> int:
         if threads > 1:
             cpu["all_cores"] = cpu_baseline_all_cores(x_host, w_prev_h, w_new_h,
                                                       min(args.cpu_sample, N), len(stages), threads)
+        if args.cpu_configs:
+            cpu["configs"] = cpu_baseline_configs(x_host, threads)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -581,11 +591,12 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
 
 
 def measure_compress_pattern(L, dev, x, reps=20):
-    """Each compress of the step alone on the bucket beside the reference
-    kernel with its memory volume and none of its arithmetic (reads the
-    binary32 bucket, writes the same number of code words; the scales' 2/B
-    bytes per element are not written): median of `reps`, every launch after
-    a 1 GiB read that leaves the Infinity Cache clean."""
+    """Each compress and decompress of the step alone on the bucket, and
+    beside the compress the reference kernel with its memory volume and none
+    of its arithmetic (reads the binary32 bucket, writes the same number of
+    code words; the scales' 2/B bytes per element are not written): median of
+    `reps`, every launch after a 1 GiB read that leaves the Infinity Cache
+    clean."""
     import torch
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -606,20 +617,26 @@ def measure_compress_pattern(L, dev, x, reps=20):
         return sorted(ts)[len(ts) // 2]
 
     out = {}
+    y = torch.empty(N, dtype=torch.float32, device=dev)
     for b in BITS:
         nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
         c = torch.empty(nw, dtype=torch.int32, device=dev)
         s = torch.empty(nb, dtype=torch.float16, device=dev)
         cms = alone(lambda: L.quantize_pack(x, b, BLOCK, b > 1, SEED, 0, c, s))
+        dms = alone(lambda: L.unpack_dequant(c, s, N, b, BLOCK, out=y))
         rms = alone(lambda: L.fold_f32(x, b, c))
         alg, ref = N * 4 + nw * 4 + nb * 2, N * 4 + nw * 4
-        cg, rg = alg / (cms * 1e-3) / 1e9, ref / (rms * 1e-3) / 1e9
+        cg, dg, rg = (alg / (cms * 1e-3) / 1e9, alg / (dms * 1e-3) / 1e9,
+                      ref / (rms * 1e-3) / 1e9)
         out[f"b{b}"] = {"workload": f"{N} fp32 bucket, b{b} B{BLOCK}" + (" SR" if b > 1 else ""),
                         "compress_us": round(cms * 1e3, 2), "compress_GBps": round(cg, 1),
                         "frac": round(cg / HBM_PEAK_GBS, 3),
+                        "decompress_us": round(dms * 1e3, 2), "decompress_GBps": round(dg, 1),
+                        "decompress_frac": round(dg / HBM_PEAK_GBS, 3),
                         "reference_us": round(rms * 1e3, 2), "reference_GBps": round(rg, 1),
                         "of_reference": round(cg / rg, 3)}
         del c, s
+    del y
     return out
 
 
@@ -897,6 +914,112 @@ def cpu_baseline_all_cores(x, w_prev, w_new, n, nstages, threads):
     ex.shutdown()
     return {"value": round(nstages * n * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "seconds": round(dt, 2)}
+
+
+def cpu_baseline_configs(x_bucket, threads, reps=3):
+    """The CPU oracle on each workload configuration's own operation, on the
+    host recipes the parity tests use (synth): one thread and `threads`
+    threads (block-aligned element ranges; blocks are independent and the SR
+    hash is keyed on the global index, so the outputs are the same bytes),
+    median wall time of `reps` runs (5 for the small roundtrip), excluding
+    input generation.  Sizes are the configurations' own, except the weight
+    shard (840 Mi elements), which is timed on a 64 Mi sample drawn with the
+    same recipe.  GB/s as in the GPU rows: input = full-precision bytes of the
+    operation's input as stored, alg = algorithmic bytes."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle as O
+    from weight_communication_compression_amd import synth
+
+    ex = cf.ThreadPoolExecutor(threads)
+
+    def median_s(fn, k):
+        ts = []
+        for _ in range(k):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    def par(fn, total, align):
+        return list(ex.map(lambda r: fn(*r), _block_ranges(total, align, threads)))
+
+    def entry(workload, n, input_bytes, alg_bytes, one, many, k=reps):
+        t1, tm = median_s(one, k), median_s(many, k)
+        row = lambda t: {"s": round(t, 4), "input_GBps": round(input_bytes / t / 1e9, 3),
+                         "alg_GBps": round(alg_bytes / t / 1e9, 3)}
+        return {"workload": workload, "elements": n, "reps": k, "stat": "median",
+                "one_thread": row(t1), "all_threads": dict(threads=threads, **row(tm))}
+
+    nwb = lambda n, b: O.num_words(n, b) * 4
+    nbb = lambda n, B: O.num_blocks(n, B) * 2
+    out = {}
+
+    # roundtrip: 2^20 fp32 N(0,1), b4 B128 nearest, compress then decompress
+    x = synth.roundtrip_input()
+    n = x.size
+
+    def rt(lo, hi):
+        c, s = O.quantize_pack(x[lo:hi], 4, 128, False, 0, lo)
+        O.unpack_dequant(c, s, hi - lo, 4, 128)
+    out["roundtrip 2^20 fp32 b4 B128"] = entry(
+        f"{n} fp32 N(0,1), b4 B128 nearest: compress + decompress", n, n * 4,
+        2 * (n * 4 + nwb(n, 4) + nbb(n, 128)), lambda: rt(0, n),
+        lambda: par(rt, n, 32 * 128), k=5)
+
+    # gradient bucket: 64 Mi fp32 Student-t(3) x 1e-3, B256, SR seed 42, each width
+    x = x_bucket
+    n = x.size
+    for b in BITS:
+        out[f"bucket 64Mi fp32 b{b}"] = entry(
+            f"{n} fp32 1e-3 Student-t(3), b{b} B256" + (" SR seed 42" if b > 1 else ""), n,
+            n * 4, n * 4 + nwb(n, b) + nbb(n, 256),
+            lambda b=b: O.quantize_pack(x, b, 256, True, 42, 0),
+            lambda b=b: par(lambda lo, hi: O.quantize_pack(x[lo:hi], b, 256, True, 42, lo), n,
+                            32 * 256))
+
+    # error feedback, step 0: 128 Mi bf16 1e-4 N(0,1), fp32 residual 0, b4 B128 SR seed 2
+    g = synth.ef_gradient(0)
+    n = g.size
+    e0 = np.zeros(n, np.float32)
+    out["ef_compress 128Mi bf16 b4"] = entry(
+        f"{n} bf16 1e-4 N(0,1) + fp32 residual, b4 B128 SR seed 2 (step 0)", n, n * 2,
+        n * (2 + 4 + 4) + nwb(n, 4) + nbb(n, 128),
+        lambda: O.ef_compress(g, e0, 4, 128, True, 2, 0),
+        lambda: par(lambda lo, hi: O.ef_compress(g[lo:hi], e0[lo:hi], 4, 128, True, 2, lo), n,
+                    32 * 128))
+    del g, e0
+
+    # local reduce: 8 peers x 32 Mi, each N(0,1) (seeds 10..17) compressed b4 B128 nearest
+    n = synth.PEER_N
+    peers = list(ex.map(lambda p: O.quantize_pack(synth.peer_input(p), 4, 128),
+                        range(synth.PEERS)))
+    pc, ps = [c for c, _ in peers], [s for _, s in peers]
+
+    def red(lo, hi):
+        w0, w1 = lo * 4 // 32, O.num_words(hi, 4)
+        O.reduce_requant([c[w0:w1] for c in pc],
+                         [s[lo // 128:O.num_blocks(hi, 128)] for s in ps], hi - lo, 4, 128, 4)
+    out["reduce_requant 8x32Mi b4"] = entry(
+        f"8 x {n} peers, b4 B128 -> b4 B128 nearest", n, synth.PEERS * n * 4,
+        (synth.PEERS + 1) * (nwb(n, 4) + nbb(n, 128)), lambda: red(0, n),
+        lambda: par(red, n, 32 * 128))
+    del peers, pc, ps
+
+    # weight difference: 64 Mi sample of the bf16 shard recipe, b4 B64 compress + apply
+    n = 64 << 20
+    wp, wn = synth.weight_pair(n)
+
+    def wd(lo, hi):
+        c, s = O.wdiff_compress(wn[lo:hi], wp[lo:hi], 4, 64)
+        O.wdiff_apply(wp[lo:hi], c, s, 4, 64)
+    out["wdiff 840Mi bf16 b4 (64Mi sample)"] = entry(
+        f"{n}-element sample of the 840 Mi bf16 shard recipe, b4 B64 nearest: "
+        "compress + apply", n, 2 * n * 2 + n * 2,
+        2 * (2 * n * 2 + nwb(n, 4) + nbb(n, 64)), lambda: wd(0, n),
+        lambda: par(wd, n, 32 * 64))
+    ex.shutdown()
+    return out
 
 
 def cpu_baseline(x, w_prev, w_new, n, nstages):

@@ -90,12 +90,22 @@ typedef enum {
 
 /* Quantizer options (bitscom README, "Backend Registration Options": bitwidth
  * and block size; "Implemented Features": stochastic rounding). */
+
+/* lowbit_qparams.hints: the caller reads the compress input again soon (for
+ * example it compresses the same buffer at another bitwidth next): keep it in
+ * the caches.  Without it a compress streams its input where its access
+ * pattern allows (non-temporal loads: binary32 input at 1 and 8 bits in the
+ * plain compress), which is faster for a buffer compressed once.  Accepted by
+ * every entry point; the others ignore it. */
+#define LOWBIT_HINT_INPUT_REUSED 1
 typedef struct {
     int32_t  bitwidth;        /* b: 1, 2, 4 or 8                                */
     int32_t  block_size;      /* B: power of two in [32, 4096]                  */
     int32_t  stochastic;      /* 0: nearest, ties to even; 1: stochastic
                                  rounding (ignored when b == 1)                 */
-    int32_t  reserved;        /* must be 0                                      */
+    int32_t  hints;           /* cache hints, LOWBIT_HINT_* bits (0: none); they
+                                 change how data moves through the caches,
+                                 never a result                                 */
     uint64_t seed;            /* stochastic-rounding key                        */
     uint64_t index_offset;    /* global index of element 0; a multiple of B.
                                  Only the random numbers depend on it, so a
@@ -119,8 +129,8 @@ const char* lowbit_version(void);
  *   x      : device, n elements of type xt
  *   codes  : device, lowbit_num_words(n, p->bitwidth) words (written)
  *   scales : device, lowbit_num_blocks(n, p->block_size) binary16 (written)
- * EINVAL: p == NULL, bad bitwidth/block_size/reserved, index_offset not a
- * multiple of block_size, n < 0, NULL or misaligned pointer with n > 0,
+ * EINVAL: p == NULL, bad bitwidth/block_size, unknown hint bits, index_offset
+ * not a multiple of block_size, n < 0, NULL or misaligned pointer with n > 0,
  * unknown dtype.
  */
 lowbit_status lowbit_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,

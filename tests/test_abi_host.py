@@ -59,13 +59,13 @@ def test_size_helpers_reject():
 
 
 def _qp(**kw):
-    d = dict(bitwidth=4, block_size=128, stochastic=0, reserved=0, seed=0, index_offset=0)
+    d = dict(bitwidth=4, block_size=128, stochastic=0, hints=0, seed=0, index_offset=0)
     d.update(kw)
     return lb.QParams(**d)
 
 
 BAD_PARAMS = [dict(bitwidth=3), dict(bitwidth=16), dict(block_size=16), dict(block_size=96),
-              dict(block_size=8192), dict(index_offset=64), dict(reserved=1)]
+              dict(block_size=8192), dict(index_offset=64), dict(hints=2), dict(hints=-1)]
 
 
 @pytest.mark.parametrize("bad", BAD_PARAMS)

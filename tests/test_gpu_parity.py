@@ -46,6 +46,27 @@ def _device():
 
 
 # -------------------------------------------------------------- compress --
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("B", [32, 256, 4096])
+@pytest.mark.parametrize("bits", BITS)
+def test_quantize_input_reused_hint(bits, B, sr):
+    """LOWBIT_HINT_INPUT_REUSED selects cached rather than streamed loads of
+    the input (1 and 8 bits, binary32); the codes and scales are the same."""
+    for i, n in enumerate(_sizes(bits, B)):
+        x = _input("mixed", n, 7000 * bits + B + i, "f32")
+        say(f"quantize (input reused) bits={bits} B={B} sr={sr} n={n}")
+        gx = to_gpu(x)
+        c, s = L.quantize_pack(gx, bits, B, sr, 5, B * i, input_reused=True)
+        c2, s2 = L.quantize_pack(gx, bits, B, sr, 5, B * i, input_reused=False)
+        torch.cuda.synchronize()
+        wc, ws = O.quantize_pack(x, bits, B, sr, 5, B * i)
+        assert_same(scales_np(s), ws, f"scales n={n}")
+        assert_same(codes_np(c), wc, f"codes n={n}")
+        assert_same(scales_np(s2), ws, f"scales n={n}")
+        assert_same(codes_np(c2), wc, f"codes n={n}")
+
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("sr", [False, True])
 @pytest.mark.parametrize("B", BLOCKS)

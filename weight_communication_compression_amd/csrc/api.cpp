@@ -1,11 +1,9 @@
 // api.cpp -- the extern "C" entry points of liblowbit (declared in
 // include/lowbit.h): argument validation, the stochastic-rounding key, and
 // dispatch to the gfx950 kernels.  Invalid arguments are rejected before any
-// HIP call; nothing here allocates device memory or keeps state other than a
-// per-device cache of the compute-unit count.
+// HIP call; nothing here allocates device memory or keeps any state.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <stdint.h>
 
 #include "../../include/lowbit.h"
@@ -15,9 +13,6 @@
 namespace lowbit {
 
 namespace {
-
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];
 
 constexpr int64_t kMaxN = (int64_t)1 << 48;
 
@@ -48,7 +43,7 @@ uint32_t seed_key(uint64_t seed) {
 
 // Common checks of one lowbit_qparams; returns log2(B) or -1.
 int check_params(const lowbit_qparams* p) {
-  if (!p || !valid_bits(p->bitwidth) || p->reserved != 0) return -1;
+  if (!p || !valid_bits(p->bitwidth) || (p->hints & ~LOWBIT_HINT_INPUT_REUSED) != 0) return -1;
   const int lb = log2_block(p->block_size);
   if (lb < 0) return -1;
   if (p->index_offset % (uint64_t)p->block_size != 0) return -1;
@@ -58,19 +53,6 @@ int check_params(const lowbit_qparams* p) {
 bool valid_dtype(int dt) { return dt == LOWBIT_F32 || dt == LOWBIT_BF16; }
 
 }  // namespace
-
-int device_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  int c = g_cu_count[dev].load(std::memory_order_relaxed);
-  if (c <= 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        c <= 0)
-      c = 256;
-    g_cu_count[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
 
 }  // namespace lowbit
 
@@ -112,7 +94,8 @@ lowbit_status lowbit_quantize_pack(const void* x, lowbit_dtype xt, int64_t n,
   a.x = x;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_plain(p->bitwidth, lb, p->stochastic != 0, (int)xt, a, stream);
+  return launch_quantize_plain(p->bitwidth, lb, p->stochastic != 0, (int)xt,
+                               (p->hints & LOWBIT_HINT_INPUT_REUSED) == 0, a, stream);
 }
 
 lowbit_status lowbit_unpack_dequant(const uint32_t* codes, const uint16_t* scales, int64_t n,
@@ -144,7 +127,7 @@ lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int6
   a.x = x;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_hadamard(p->bitwidth, lb, p->stochastic != 0, (int)xt, a, stream);
+  return launch_quantize_hadamard(p->bitwidth, lb, p->stochastic != 0, (int)xt, false, a, stream);
 }
 
 lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales,
@@ -178,7 +161,7 @@ lowbit_status lowbit_ef_compress(const void* g, lowbit_dtype gt, float* residual
   a.resid = residual;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_ef(p->bitwidth, lb, p->stochastic != 0, (int)gt, a, stream);
+  return launch_quantize_ef(p->bitwidth, lb, p->stochastic != 0, (int)gt, false, a, stream);
 }
 
 }  // extern "C"
@@ -264,7 +247,7 @@ lowbit_status lowbit_ef21_compress(const void* g, lowbit_dtype gt, float* state,
   a.resid = state;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_ef21(p->bitwidth, lb, p->stochastic != 0, (int)gt, a, stream);
+  return launch_quantize_ef21(p->bitwidth, lb, p->stochastic != 0, (int)gt, false, a, stream);
 }
 
 lowbit_status lowbit_wdiff_compress(const void* w_new, const void* w_old, lowbit_dtype wt,
@@ -281,7 +264,7 @@ lowbit_status lowbit_wdiff_compress(const void* w_new, const void* w_old, lowbit
   a.x2 = w_old;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_wdiff(p->bitwidth, lb, p->stochastic != 0, (int)wt, a, stream);
+  return launch_quantize_wdiff(p->bitwidth, lb, p->stochastic != 0, (int)wt, false, a, stream);
 }
 
 lowbit_status lowbit_wdiff_apply(const void* w_old, const uint32_t* codes, const uint16_t* scales,

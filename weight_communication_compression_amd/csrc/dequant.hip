@@ -10,9 +10,8 @@ static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
   constexpr int ROW = kWave * dequant_epl<APPLY>();
   const int64_t nrows = (a.n + ROW - 1) / ROW;
   const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
-  hipLaunchKernelGGL((dequant_kernel<BITS, APPLY, DT>), dim3(grid_for_tiles<kDeqThreads>(ntrips)),
-                     dim3(kDeqThreads), 0, s, a);
-  return launch_status();
+  return launch(&dequant_kernel<BITS, APPLY, DT>, grid_for_tiles<kDeqThreads>(ntrips), kDeqThreads,
+                s, a);
 }
 
 template <int BITS>
@@ -35,11 +34,9 @@ template <int BITS, int LOG2B>
 static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   constexpr int ROWS = hadamard_rows_per_trip<LOG2B>();
-  // one wave per LOWBIT_HS_DEQ_TRIPS trips
-  const int64_t waves = (nrows + ROWS * LOWBIT_HS_DEQ_TRIPS - 1) / (ROWS * LOWBIT_HS_DEQ_TRIPS);
-  hipLaunchKernelGGL((hadamard_dequant_kernel<BITS, LOG2B>),
-                     dim3(grid_for_tiles<kDeqThreads>(waves)), dim3(kDeqThreads), 0, s, a);
-  return launch_status();
+  const int64_t waves = (nrows + ROWS - 1) / ROWS;   // one trip per wave
+  return launch(&hadamard_dequant_kernel<BITS, LOG2B>, grid_for_tiles<kDeqThreads>(waves),
+                kDeqThreads, s, a);
 }
 
 template <int BITS>
@@ -69,34 +66,26 @@ lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_
 
 lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s) {
   const int64_t nvec = n / 4;
-  int64_t blocks = (nvec + kCopyUnroll * kBlockThreads - 1) / (kCopyUnroll * kBlockThreads);
-  int64_t cap = (int64_t)1 << 30;
-  if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, x, y, n);
-  return launch_status();
+  return launch(&copy_kernel, grid_blocks((nvec + 63) / 64, kBlockThreads), kBlockThreads, s, x, y,
+                n);
 }
 
 lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s) {
   const int64_t waves = (n + 4 * kWave - 1) / (4 * kWave);
-  hipLaunchKernelGGL(add_inplace_kernel, dim3(grid_for_tiles(waves)), dim3(kBlockThreads), 0, s,
-                     x, y, n);
-  return launch_status();
+  return launch(&add_inplace_kernel, grid_for_tiles(waves), kBlockThreads, s, x, y, n);
 }
 
 lowbit_status launch_fold(const float* x, int64_t n, int bits, uint32_t* out, hipStream_t s) {
   const int64_t tiles = (n + 2047) / 2048;
   const int64_t nwords = (n * bits + 31) / 32;
-  const dim3 grid(grid_for_tiles(tiles)), block(kBlockThreads);
+  const int64_t grid = grid_for_tiles(tiles);
   switch (bits) {
-    case 1: hipLaunchKernelGGL(fold_kernel<1>, grid, block, 0, s, x, n, out, nwords); break;
-    case 2: hipLaunchKernelGGL(fold_kernel<2>, grid, block, 0, s, x, n, out, nwords); break;
-    case 4: hipLaunchKernelGGL(fold_kernel<4>, grid, block, 0, s, x, n, out, nwords); break;
-    case 8: hipLaunchKernelGGL(fold_kernel<8>, grid, block, 0, s, x, n, out, nwords); break;
-    default: return LOWBIT_EUNSUPPORTED;
+    case 1: return launch(&fold_kernel<1>, grid, kBlockThreads, s, x, n, out, nwords);
+    case 2: return launch(&fold_kernel<2>, grid, kBlockThreads, s, x, n, out, nwords);
+    case 4: return launch(&fold_kernel<4>, grid, kBlockThreads, s, x, n, out, nwords);
+    case 8: return launch(&fold_kernel<8>, grid, kBlockThreads, s, x, n, out, nwords);
   }
-  return launch_status();
+  return LOWBIT_EUNSUPPORTED;
 }
 
 }  // namespace lowbit

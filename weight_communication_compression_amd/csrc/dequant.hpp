@@ -24,22 +24,14 @@ namespace lowbit {
 // decompresses from 201 to 184 us against 8 rows (4 rows: 200 us, 1 row:
 // slower); with the Infinity Cache flushed first, 2 rows is 12 % faster at
 // 8 bits and 5 % slower at 1 and 2 bits.
-#ifndef LOWBIT_DEQ_ROWS
-#define LOWBIT_DEQ_ROWS 2
-#endif
-#ifndef LOWBIT_APPLY_ROWS
-#define LOWBIT_APPLY_ROWS 2
-#endif
-#ifndef LOWBIT_DEQ_EPL
-#define LOWBIT_DEQ_EPL 4
-#endif
-#ifndef LOWBIT_APPLY_EPL
-#define LOWBIT_APPLY_EPL 8
-#endif
+constexpr int kDeqRows = 2;
+constexpr int kApplyRows = 2;
+constexpr int kDeqEpl = 4;
+constexpr int kApplyEpl = 8;
 template <int APPLY>
-constexpr int dequant_rows() { return APPLY ? LOWBIT_APPLY_ROWS : LOWBIT_DEQ_ROWS; }
+constexpr int dequant_rows() { return APPLY ? kApplyRows : kDeqRows; }
 template <int APPLY>
-constexpr int dequant_epl() { return APPLY ? LOWBIT_APPLY_EPL : LOWBIT_DEQ_EPL; }
+constexpr int dequant_epl() { return APPLY ? kApplyEpl : kDeqEpl; }
 constexpr int kDeqRow = kWave * 4;              // elements per row at 4 per lane
 
 // Decode the N codes in bits [off, off + N*b) of `word` with scale s
@@ -160,16 +152,18 @@ __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
   const int64_t wave = global_wave_id<kDeqThreads>();
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t nrows = (a.n + ROW - 1) / ROW;
-  for (int64_t base = wave * kDequantRows; base < nrows; base += nwaves * kDequantRows) {
+  const int64_t ntrips = (nrows + kDequantRows - 1) / kDequantRows;
+  for_each_trip(wave, ntrips, nwaves, [&](int64_t t) __attribute__((always_inline)) {
+    const int64_t base = t * kDequantRows;
     // wave-uniform: every trip but the last lies inside the buffer
     if ((base + kDequantRows) * ROW <= a.n) dequant_trip<BITS, APPLY, DT, false>(a, base);
     else dequant_trip<BITS, APPLY, DT, true>(a, base);
-  }
+  });
 }
 
 // Decompress followed by the inverse blockwise Walsh-Hadamard transform
 // (blocks of B = 2^LOG2B elements).  Same element-centric layout (rows of
-// 256, 4 elements per lane); a trip of max(LOWBIT_HS_DEQ_ROWS, B/256) rows
+// 256, 4 elements per lane); a trip of max(8, B/256) rows
 // holds whole blocks, so the transform runs in registers: elements within
 // the lane, then lanes, then rows.  Loads and stores are guarded, the
 // transform is not (every lane of the wave takes part in the exchanges;
@@ -177,20 +171,11 @@ __global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
 // measured on the 64 Mi bucket at 4 bits, B = 128: 1 row 83 us, 2: 65,
 // 4: 63, 8: 60.6, 16: 75 (more rows keep more exchanges in flight per wave
 // until the register footprint costs occupancy).
-#ifndef LOWBIT_HS_DEQ_ROWS
-#define LOWBIT_HS_DEQ_ROWS 8
-#endif
+constexpr int kHsDeqRows = 8;
 template <int LOG2B>
 constexpr int hadamard_rows_per_trip() {
-  return (1 << LOG2B) > LOWBIT_HS_DEQ_ROWS * kDeqRow ? (1 << LOG2B) / kDeqRow : LOWBIT_HS_DEQ_ROWS;
+  return (1 << LOG2B) > kHsDeqRows * kDeqRow ? (1 << LOG2B) / kDeqRow : kHsDeqRows;
 }
-
-// Trips per wave of the decompress with inverse smoothing: with 2, a wave
-// issues the code and scale loads of both trips before transforming the
-// first (measured on the 64 Mi bucket, b4: 61 us against 58 with 1).
-#ifndef LOWBIT_HS_DEQ_TRIPS
-#define LOWBIT_HS_DEQ_TRIPS 1
-#endif
 
 // Code words and scales of one trip (rows base .. base + rows - 1).  GUARD:
 // the trip may reach past n (the last one only).
@@ -252,52 +237,33 @@ template <int BITS, int LOG2B>
 __global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
   constexpr int B = 1 << LOG2B;
   constexpr int R = hadamard_rows_per_trip<LOG2B>();
-  constexpr int T = LOWBIT_HS_DEQ_TRIPS;
   static_assert(B <= R * kDeqRow, "a block must fit in one trip");
   const int64_t wave = global_wave_id<kDeqThreads>();
   const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   const int64_t ntrips = (nrows + R - 1) / R;
-  for (int64_t t = wave * T; t < ntrips; t += nwaves * T) {
+  for_each_trip(wave, ntrips, nwaves, [&](int64_t t) __attribute__((always_inline)) {
+    uint32_t word[R], s16[R];
     // wave-uniform: every trip but the last lies inside the buffer
-    if ((t + T) * R * kDeqRow <= a.n) {
-      uint32_t word[T][R], s16[T][R];
-#pragma unroll
-      for (int k = 0; k < T; ++k)
-        hadamard_dequant_load<BITS, LOG2B, false>(a, (t + k) * R, word[k], s16[k]);
-#pragma unroll
-      for (int k = 0; k < T; ++k)
-        hadamard_dequant_finish<BITS, LOG2B, false>(a, (t + k) * R, word[k], s16[k]);
+    if ((t + 1) * R * kDeqRow <= a.n) {
+      hadamard_dequant_load<BITS, LOG2B, false>(a, t * R, word, s16);
+      hadamard_dequant_finish<BITS, LOG2B, false>(a, t * R, word, s16);
     } else {
-      for (int k = 0; k < T && t + k < ntrips; ++k) {
-        uint32_t word[R], s16[R];
-        hadamard_dequant_load<BITS, LOG2B, true>(a, (t + k) * R, word, s16);
-        hadamard_dequant_finish<BITS, LOG2B, true>(a, (t + k) * R, word, s16);
-      }
+      hadamard_dequant_load<BITS, LOG2B, true>(a, t * R, word, s16);
+      hadamard_dequant_finish<BITS, LOG2B, true>(a, t * R, word, s16);
     }
-  }
+  });
 }
 
-#ifndef LOWBIT_COPY_UNROLL
-#define LOWBIT_COPY_UNROLL 1
-#endif
-constexpr int kCopyUnroll = LOWBIT_COPY_UNROLL;
-
-// Plain binary32 copy with the codec kernels' launch shape (measurement aid).
+// Plain binary32 copy with the codec kernels' launch shape (measurement aid):
+// one float4 per thread and trip.
 __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, float* y, int64_t n) {
   const int64_t nvec = n / 4;
   const int64_t stride = (int64_t)gridDim.x * kBlockThreads;
   const float4* xv = reinterpret_cast<const float4*>(x);
   float4* yv = reinterpret_cast<float4*>(y);
-  int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-  for (; i + (kCopyUnroll - 1) * stride < nvec; i += kCopyUnroll * stride) {
-    float4 t[kCopyUnroll];
-#pragma unroll
-    for (int k = 0; k < kCopyUnroll; ++k) t[k] = xv[i + k * stride];
-#pragma unroll
-    for (int k = 0; k < kCopyUnroll; ++k) yv[i + k * stride] = t[k];
-  }
-  for (; i < nvec; i += stride) yv[i] = xv[i];
+  for (int64_t i = logical_block() * kBlockThreads + threadIdx.x; i < nvec; i += stride)
+    yv[i] = xv[i];
   const int64_t t = nvec * 4 + (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (t < n) y[t] = x[t];
 }
@@ -310,22 +276,23 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, flo
 __global__ __launch_bounds__(kBlockThreads) void add_inplace_kernel(const float* x, float* y,
                                                                     int64_t n) {
   constexpr int E = 4, CHUNK = kWave * E;
-  const int64_t t0 = global_wave_id() * CHUNK;              // wave-uniform
-  if (t0 >= n) return;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const uint32_t off = (uint32_t)lane_id() * E;
-  float a[E], b[E];
-  if (t0 + CHUNK <= n) {
-    load_vec<kF32, E>(x, t0, off, a);
-    load_vec<kF32, E>(y, t0, off, b);
+  for (int64_t t0 = global_wave_id() * CHUNK; t0 < n; t0 += nwaves * CHUNK) {   // wave-uniform
+    float a[E], b[E];
+    if (t0 + CHUNK <= n) {
+      load_vec<kF32, E>(x, t0, off, a);
+      load_vec<kF32, E>(y, t0, off, b);
 #pragma unroll
-    for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
-    store_vec_f32<E>(y, t0, off, b);
-  } else {
-    load_tail<kF32, E>(x, t0, off, n - t0, a);
-    load_tail<kF32, E>(y, t0, off, n - t0, b);
+      for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
+      store_vec_f32<E>(y, t0, off, b);
+    } else {
+      load_tail<kF32, E>(x, t0, off, n - t0, a);
+      load_tail<kF32, E>(y, t0, off, n - t0, b);
 #pragma unroll
-    for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
-    store_tail_f32<E>(y, t0, off, n - t0, b);
+      for (int j = 0; j < E; ++j) b[j] = b[j] + a[j];
+      store_tail_f32<E>(y, t0, off, n - t0, b);
+    }
   }
 }
 

@@ -12,20 +12,11 @@
 namespace lowbit {
 
 constexpr int kWave = 64;
-#ifndef LOWBIT_BLOCK_THREADS
-#define LOWBIT_BLOCK_THREADS 256
-#endif
-constexpr int kBlockThreads = LOWBIT_BLOCK_THREADS;   // threads per workgroup
+constexpr int kBlockThreads = 256;   // threads per workgroup
 // the decompress kernels' workgroup size (stores dominate; smaller groups
 // start and retire in finer steps)
-#ifndef LOWBIT_DEQ_BLOCK_THREADS
-#define LOWBIT_DEQ_BLOCK_THREADS 128
-#endif
-constexpr int kDeqThreads = LOWBIT_DEQ_BLOCK_THREADS;
-#ifndef LOWBIT_XCD_REMAP
-#define LOWBIT_XCD_REMAP 0
-#endif
-constexpr int kXcds = 8;                              // MI355X: 8 XCDs of 32 CUs
+constexpr int kDeqThreads = 128;
+constexpr int kXcds = 8;             // MI355X: 8 XCDs of 32 CUs, one L2 each
 constexpr float kMagic = 12582912.0f;           // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;    // bit pattern of kMagic
 
@@ -58,57 +49,69 @@ struct Grid {
 };
 
 // Per-lane elements a wave loads per loop trip: nearest rounding is light on
-// ALU and prefers short trips; stochastic rounding hides its hashing better
-// with a second tile's loads in flight.
-#ifndef LOWBIT_ELEMS_PER_TRIP
-#define LOWBIT_ELEMS_PER_TRIP 8
-#endif
-#ifndef LOWBIT_SR_ELEMS_PER_TRIP
-#define LOWBIT_SR_ELEMS_PER_TRIP 16
-#endif
-#ifndef LOWBIT_BF16_ELEMS_PER_TRIP
-#define LOWBIT_BF16_ELEMS_PER_TRIP 8
-#endif
+// ALU and prefers short trips; stochastic rounding of 8-bit codes (four
+// elements per lane and tile) hides its hashing better with more tiles' loads
+// in flight.  Measured on the 64 Mi bucket, each compress alone: 8 bits, 16
+// elements 61.6 us, 8 elements 65.8 us; 4 bits, 16 elements 55.6 us, 8
+// elements 52.8 us (inside the whole-path step 52.0 and 50.1 us).
+constexpr int kElemsPerTrip = 8;
+constexpr int kSrElemsPerTrip = 16;
 
 // Tiles per loop trip for a kernel whose tile gives each lane PER_LANE
-// elements (bfloat16 inputs may ask for more elements per trip: half the bytes).
-template <int PER_LANE, bool SR = false, bool HALF = false>
+// elements: enough tiles for kElemsPerTrip elements, or with stochastic
+// rounding for kSrElemsPerTrip when a tile gives a lane fewer than 8.
+template <int PER_LANE, bool SR = false>
 constexpr int tiles_per_trip() {
-  constexpr int base = SR ? LOWBIT_SR_ELEMS_PER_TRIP : LOWBIT_ELEMS_PER_TRIP;
-  constexpr int want = HALF && LOWBIT_BF16_ELEMS_PER_TRIP > base ? LOWBIT_BF16_ELEMS_PER_TRIP : base;
+  constexpr int want = SR && PER_LANE < 8 ? kSrElemsPerTrip : kElemsPerTrip;
   return PER_LANE >= want ? 1 : want / PER_LANE;
 }
-
-// Non-temporal hint on the large outputs (decompressed values, residuals,
-// sums, packed codes, applied weights): written through rather than parked
-// dirty in the Infinity Cache, where the next kernel would pay for their
-// write-back (measured: +12 % on a whole compress/reduce/decompress/EF/
-// weight-diff pass).
-#ifndef LOWBIT_NT_STORES
-#define LOWBIT_NT_STORES 1
-#endif
 
 // ---------------------------------------------------------------- lanes --
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroups are dealt to the XCDs round-robin (hardware workgroup b runs on
+// XCD b mod 8), and each XCD has its own L2.  Where neighbouring workgroups
+// share cache lines (the binary16 scales of several tiles), runs of CHUNK
+// consecutive logical workgroups can be given to one XCD: within each whole
+// group of 8 * CHUNK workgroups, workgroup b takes logical workgroup
+// (b mod 8) * CHUNK + (b / 8) mod CHUNK.  A group is still one contiguous
+// stretch of memory, so HBM keeps seeing a single stream; a trailing partial
+// group keeps the identity mapping.  The map is a bijection on
+// [0, gridDim.x).  CHUNK = 1: the hardware order.
+template <int CHUNK = 1>
+__device__ __forceinline__ int64_t logical_block() {
+  const int64_t b = blockIdx.x;
+  if constexpr (CHUNK <= 1) {
+    return b;
+  } else {
+    constexpr int64_t G = (int64_t)kXcds * CHUNK;
+    const int64_t whole = ((int64_t)gridDim.x / G) * G;
+    if (b >= whole) return b;
+    const int64_t r = b % G;
+    return b - r + (r % kXcds) * CHUNK + r / kXcds;
+  }
+}
+
 // Index of this wave in the grid, as a wave-uniform (scalar) value: element
 // offsets then split into a scalar base and a 32-bit per-lane offset, and
 // loads and stores use the scalar-base addressing mode.  THREADS: the
-// kernel's workgroup size.
-template <int THREADS = kBlockThreads>
+// kernel's workgroup size; CHUNK: see logical_block.
+template <int THREADS = kBlockThreads, int CHUNK = 1>
 __device__ __forceinline__ int64_t global_wave_id() {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  int64_t b = blockIdx.x;
-  if (LOWBIT_XCD_REMAP) {
-    // workgroups are dealt to the XCDs round-robin (b % 8); give each XCD one
-    // contiguous range of the work instead, so neighbouring tiles (and the
-    // cache lines of codes and scales they share) stay in one L2
-    const int64_t nb = gridDim.x;
-    const int64_t q = nb / kXcds, r = nb % kXcds;
-    const int64_t x = b % kXcds, i = b / kXcds;
-    b = x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-  }
-  return b * (THREADS / kWave) + w;
+  return logical_block<CHUNK>() * (THREADS / kWave) + w;
+}
+
+// body(i) for i = first, first + stride, ... below count.  The grid gives
+// every wave one trip unless it was capped (more than 2^32 work-items), so
+// the first call is kept out of the loop: its addresses are then offsets from
+// kernel arguments rather than values carried from iteration to iteration in
+// 64-bit vector registers.
+template <typename F>
+__device__ __forceinline__ void for_each_trip(int64_t first, int64_t count, int64_t stride,
+                                              F&& body) {
+  if (first < count) body(first);
+  for (int64_t i = first + stride; i < count; i += stride) body(i);
 }
 
 template <int CTRL>
@@ -293,36 +296,24 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // element offset `off`, which maps onto the scalar-base + 32-bit-offset
 // addressing mode of global loads and stores.
 
-// Non-temporal loads in the error-feedback compresses: 0 none, 1 the
-// residual/state (rewritten in place), 2 the gradient too.  Measured on the
-// 64 Mi bucket step: with 1, the EF compress no longer leaves dirty residual
-// lines in the Infinity Cache (the kernel after it runs 15 us faster) but is
-// itself 18 us slower (149 vs 131 us); the step gains 1 %.  0 keeps the EF
-// compress, the largest kernel of the step, at its own best rate.
-#ifndef LOWBIT_EF_NT_LOADS
-#define LOWBIT_EF_NT_LOADS 0
-#endif
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Non-temporal loads of the plain compress's binary32 input where a wave's
-// 16-byte loads cover consecutive 16-byte pieces (the 1-bit compress, and
-// the 8-bit one with 4 elements per lane).  Measured on the 64 Mi bucket:
-// alone, 1 bit 50.4 -> 47 us and 8 bits 61.4 -> 59 us; but a later kernel
-// that reads the same input then finds none of it in the Infinity Cache
-// (in the whole-path step the 2-bit compress after the 1-bit chain goes
-// from 50 to 59 us and the step from 0.633 to 0.663 ms), so the default
-// keeps plain loads.  Where a lane's elements span several 16-byte pieces
-// (2 and 4 bits: 64- and 32-byte lane strides) the hint costs up to 50 %
-// and is never applied.
-#ifndef LOWBIT_X_NT_LOADS
-#define LOWBIT_X_NT_LOADS 0
-#endif
-// Non-temporal loads of the peers' code words in the local reduce (off: the
-// 8 x 32 Mi reduce gains 2-4 %, but each decompress after a reduce in the
-// step loses 10 us).
-#ifndef LOWBIT_REDUCE_NT_LOADS
-#define LOWBIT_REDUCE_NT_LOADS 0
-#endif
+// A plain compress of binary32 input reads it as a stream (non-temporal
+// loads) unless the caller says it reads the input again soon
+// (LOWBIT_HINT_INPUT_REUSED), wherever a wave's 16-byte loads cover
+// consecutive 16-byte pieces: the 1-bit compress and the 8-bit one (four
+// elements per lane).  Measured on the 64 Mi bucket, each alone after the
+// Infinity Cache was cleared: 1 bit 50.6 -> 46.3 us, 8 bits 61.6 -> 59.1 us;
+// but a second compress of the same bucket right after one with
+// non-temporal loads finds none of it in the Infinity Cache (2-bit compress
+// 49 -> 57 us).  Where a lane's elements span several 16-byte pieces (2 and 4
+// bits: 64- and 32-byte lane strides) the hint costs up to 50 % (each load
+// instruction then fetches half lines that the next one refetches) and is
+// never applied.
+template <int MODE, int DT, int E>
+constexpr bool stream_capable() {
+  return MODE == kPlain && DT == kF32 && E == 4;
+}
 
 // Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8
 // in bf16 and E >= 4 in fp32; 8-byte for E == 4 in bf16); NT: non-temporal
@@ -392,10 +383,12 @@ __device__ __forceinline__ void load_tail(const void* base, int64_t t0, uint32_t
 
 // Streaming stores: outputs are written once and read by a later kernel, so
 // they are stored non-temporally and do not linger as dirty cache lines whose
-// write-back the next kernel would pay for.
+// write-back the next kernel would pay for (measured on MI355X: a 256 MiB read
+// takes 43 us after a non-temporal 256 MiB write, 66 us after a plain one;
+// the whole compress/reduce/decompress/EF/weight-difference pass is 12 %
+// faster with non-temporal outputs).
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) {
-  if (LOWBIT_NT_STORES) __builtin_nontemporal_store(v, p);
-  else *p = v;
+  __builtin_nontemporal_store(v, p);
 }
 
 // K = 2 or 4 words (8 or 16 bytes, aligned to that) in one streaming store.
@@ -406,8 +399,7 @@ __device__ __forceinline__ void store_stream_words(uint32_t* p, const uint32_t* 
   vk q;
 #pragma unroll
   for (int k = 0; k < K; ++k) q[k] = v[k];
-  if (LOWBIT_NT_STORES) __builtin_nontemporal_store(q, reinterpret_cast<vk*>(p));
-  else *reinterpret_cast<vk*>(p) = q;
+  __builtin_nontemporal_store(q, reinterpret_cast<vk*>(p));
 }
 
 template <int E>
@@ -415,12 +407,8 @@ __device__ __forceinline__ void store_vec_f32(float* base, int64_t t0, uint32_t 
   float* p = base + t0 + off;
 #pragma unroll
   for (int k = 0; k < E / 4; ++k) {
-    if (LOWBIT_NT_STORES) {
-      const f32x4 q = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
-      __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(p) + k);
-    } else {
-      reinterpret_cast<float4*>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    }
+    const f32x4 q = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+    __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(p) + k);
   }
 }
 

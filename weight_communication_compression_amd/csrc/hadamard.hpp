@@ -17,19 +17,14 @@
 
 namespace lowbit {
 
-// Exchange unit for partners 1 and 2 lanes apart: ds_swizzle (the LDS pipe,
-// leaving the vector ALU to the butterflies) or DPP (a vector-ALU move).
-#ifndef LOWBIT_HS_DPP
-#define LOWBIT_HS_DPP 0
-#endif
-
 // v[lane ^ D], D = 1 .. 32: ds_swizzle in bit-mask mode (and 0x1F, xor D)
 // within each half-wave, ds_bpermute across the halves
 template <int D>
 __device__ __forceinline__ float xor_lane(float v) {
-  if constexpr (D == 1 && LOWBIT_HS_DPP) return dpp_f32<0xB1>(v);       // quad_perm [1,0,3,2]
-  else if constexpr (D == 2 && LOWBIT_HS_DPP) return dpp_f32<0x4E>(v);  // quad_perm [2,3,0,1]
-  else if constexpr (D <= 16) return swizzle_f32<0x1F | (D << 10)>(v);
+  // (ds_swizzle uses the LDS pipe and leaves the vector ALU to the
+  // butterflies: DPP moves for partners 1 and 2 apart measured 8 % slower on
+  // the stochastic compress)
+  if constexpr (D <= 16) return swizzle_f32<0x1F | (D << 10)>(v);
   else return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, __float_as_int(v)));
 }
 

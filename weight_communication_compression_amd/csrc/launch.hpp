@@ -6,53 +6,49 @@
 #include <stdint.h>
 
 #include "../../include/lowbit.h"
+#include <type_traits>
+
 #include "args.hpp"
 #include "device.hpp"
-
-// Optional cap on the grid, in workgroups per CU (0: no cap).  Without a cap
-// every wave makes one trip through its kernel's loop: on MI355X a grid that
-// walks memory once, in order, sustains far more HBM bandwidth than a
-// persistent grid-stride loop (measured: 6.8 vs 5-6 TB/s reads, 6.9 vs
-// 4.3-5.1 TB/s writes).
-#ifndef LOWBIT_BLOCKS_PER_CU
-#define LOWBIT_BLOCKS_PER_CU 0
-#endif
+#include "grid.hpp"
 
 namespace lowbit {
 
-
-// Number of compute units of the current device (cached per device id).
-int device_cu_count();
-
-// Grid for a kernel where each wave takes `ntrips` trips' worth of work: one
-// wave per trip (4 per workgroup); the kernels loop over whatever a cap
-// leaves.  The grid stays below 2^31 workgroups.
+// Workgroups for a kernel in which each wave takes one trip of work (one wave
+// per trip); the kernels loop over whatever the cap of grid_blocks leaves.
+// (On MI355X a grid that walks memory once, in order, sustains far more HBM
+// bandwidth than a persistent grid-stride loop: measured 6.8 vs 5-6 TB/s
+// reads, 6.9 vs 4.3-5.1 TB/s writes.)
 template <int THREADS = kBlockThreads>
-inline int grid_for_tiles(int64_t ntrips) {
-  const int64_t waves_per_block = THREADS / kWave;
-  int64_t blocks = (ntrips + waves_per_block - 1) / waves_per_block;
-  int64_t cap = (int64_t)1 << 30;
-  if (LOWBIT_BLOCKS_PER_CU > 0) cap = (int64_t)device_cu_count() * LOWBIT_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  return (int)blocks;
+inline int64_t grid_for_tiles(int64_t ntrips) {
+  return grid_blocks(ntrips, THREADS);
 }
 
-inline lowbit_status launch_status() {
-  return hipGetLastError() == hipSuccess ? LOWBIT_OK : LOWBIT_EDEVICE;
+// Launch `kernel` on `s` and return the status of this launch alone: the
+// value hipLaunchKernel returns for it.  (An error left on the thread by
+// earlier, unrelated work is neither reported nor cleared.)
+template <typename... P>
+inline lowbit_status launch(void (*kernel)(P...), int64_t blocks, int threads, hipStream_t s,
+                            typename std::common_type<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel),
+                                       dim3((uint32_t)blocks), dim3((uint32_t)threads), argv, 0, s);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_EDEVICE;
 }
 
-// mode: 0 plain, 1 error feedback, 2 weight difference, 3 EF21, 4 Hadamard
-lowbit_status launch_quantize_plain(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
-                                    hipStream_t s);
-lowbit_status launch_quantize_ef(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
-                                 hipStream_t s);
-lowbit_status launch_quantize_wdiff(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
-                                    hipStream_t s);
-lowbit_status launch_quantize_ef21(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
-                                   hipStream_t s);
-lowbit_status launch_quantize_hadamard(int bits, int log2b, bool sr, int dt, const QuantArgs& a,
-                                       hipStream_t s);
+// mode: 0 plain, 1 error feedback, 2 weight difference, 3 EF21, 4 Hadamard;
+// stream_input: read x non-temporally where the kernel can (see
+// stream_capable; the other modes ignore it)
+lowbit_status launch_quantize_plain(int bits, int log2b, bool sr, int dt, bool stream_input,
+                                    const QuantArgs& a, hipStream_t s);
+lowbit_status launch_quantize_ef(int bits, int log2b, bool sr, int dt, bool stream_input,
+                                 const QuantArgs& a, hipStream_t s);
+lowbit_status launch_quantize_wdiff(int bits, int log2b, bool sr, int dt, bool stream_input,
+                                    const QuantArgs& a, hipStream_t s);
+lowbit_status launch_quantize_ef21(int bits, int log2b, bool sr, int dt, bool stream_input,
+                                   const QuantArgs& a, hipStream_t s);
+lowbit_status launch_quantize_hadamard(int bits, int log2b, bool sr, int dt, bool stream_input,
+                                       const QuantArgs& a, hipStream_t s);
 // local reduce: same width in and out, without / with a stage-2 residual;
 // mixed widths (in_bits > bits) for the pairs 8->4, 8->2, 4->2
 lowbit_status launch_reduce_same(int bits, int log2b, bool sr, const ReduceArgs& a,

@@ -23,38 +23,39 @@ lowbit_status launch_reduce_same(int bits, int log2b, bool sr, const ReduceArgs&
 // so it shows what HBM delivers for that pattern.
 __global__ __launch_bounds__(kBlockThreads) void xor_streams_kernel(XorArgs a) {
   constexpr int W = 2, G = 8;
-  const int64_t base = global_wave_id() * (W * kWave);     // wave-uniform
-  if (base >= a.nwords) return;
-  const bool full = base + W * kWave <= a.nwords;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const uint32_t lane = (uint32_t)lane_id();
-  uint32_t acc[W] = {0u, 0u};
+  for (int64_t base = global_wave_id() * (W * kWave); base < a.nwords;
+       base += nwaves * (W * kWave)) {                      // wave-uniform
+    const bool full = base + W * kWave <= a.nwords;
+    uint32_t acc[W] = {0u, 0u};
 #pragma unroll 1
-  for (int g = 0; g < a.nstreams; g += G) {
-    uint32_t v[G][W];
+    for (int g = 0; g < a.nstreams; g += G) {
+      uint32_t v[G][W];
 #pragma unroll
-    for (int q = 0; q < G; ++q)
+      for (int q = 0; q < G; ++q)
 #pragma unroll
-      for (int i = 0; i < W; ++i) {
-        const uint32_t off = (uint32_t)i * kWave + lane;
-        v[q][i] = (g + q < a.nstreams && (full || base + off < a.nwords))
-                      ? (a.streams[g + q] + base)[off] : 0u;
-      }
+        for (int i = 0; i < W; ++i) {
+          const uint32_t off = (uint32_t)i * kWave + lane;
+          v[q][i] = (g + q < a.nstreams && (full || base + off < a.nwords))
+                        ? (a.streams[g + q] + base)[off] : 0u;
+        }
 #pragma unroll
-    for (int q = 0; q < G; ++q)
+      for (int q = 0; q < G; ++q)
 #pragma unroll
-      for (int i = 0; i < W; ++i) acc[i] ^= v[q][i];
-  }
+        for (int i = 0; i < W; ++i) acc[i] ^= v[q][i];
+    }
 #pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const uint32_t off = (uint32_t)i * kWave + lane;
-    if (full || base + off < a.nwords) store_stream(a.out + base + off, acc[i]);
+    for (int i = 0; i < W; ++i) {
+      const uint32_t off = (uint32_t)i * kWave + lane;
+      if (full || base + off < a.nwords) store_stream(a.out + base + off, acc[i]);
+    }
   }
 }
 
 lowbit_status launch_xor_streams(const XorArgs& a, hipStream_t s) {
   const int64_t waves = (a.nwords + 2 * kWave - 1) / (2 * kWave);
-  hipLaunchKernelGGL(xor_streams_kernel, dim3(grid_for_tiles(waves)), dim3(kBlockThreads), 0, s, a);
-  return launch_status();
+  return launch(&xor_streams_kernel, grid_for_tiles(waves), kBlockThreads, s, a);
 }
 
 }  // namespace lowbit

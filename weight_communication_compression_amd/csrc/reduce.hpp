@@ -18,13 +18,12 @@
 
 namespace lowbit {
 
-#ifndef LOWBIT_REDUCE_ELEMS_PER_TRIP
-#define LOWBIT_REDUCE_ELEMS_PER_TRIP 16
-#endif
+// output elements per lane per trip (8, 16 or 32 measured within noise)
+constexpr int kReduceElemsPerTrip = 16;
 
 template <int PER_LANE>
 constexpr int reduce_tiles_per_trip() {
-  return PER_LANE >= LOWBIT_REDUCE_ELEMS_PER_TRIP ? 1 : LOWBIT_REDUCE_ELEMS_PER_TRIP / PER_LANE;
+  return PER_LANE >= kReduceElemsPerTrip ? 1 : kReduceElemsPerTrip / PER_LANE;
 }
 
 // Power of two by which the reduce accumulates: each b-bit code is moved to
@@ -73,17 +72,17 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   if constexpr (M == 1) {
-    w[0] = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(p) : *p;
+    w[0] = *p;
   } else if constexpr (M == 2) {
     const u32x2* q = reinterpret_cast<const u32x2*>(p);
-    const u32x2 t = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
+    const u32x2 t = *q;
     w[0] = t.x;
     w[1] = t.y;
   } else {
 #pragma unroll
     for (int k = 0; k < M / 4; ++k) {
       const u32x4* q = reinterpret_cast<const u32x4*>(p) + k;
-      const u32x4 t = LOWBIT_REDUCE_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
+      const u32x4 t = *q;
       w[4 * k + 0] = t.x;
       w[4 * k + 1] = t.y;
       w[4 * k + 2] = t.z;
@@ -99,31 +98,49 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
 // scalar loads).  G is 8, fewer when a lane's share of a trip is large, so
 // that at most 32 loaded words per lane are held at once.  GUARD: some slots
 // of the trip lie past the end of the buffer (read as 0).
-#ifndef LOWBIT_PEER_GROUP
-#define LOWBIT_PEER_GROUP 8
-#endif
+constexpr int kPeerGroup = 8;
 template <int W, int M>
 constexpr int peer_group() {
-  constexpr int G = LOWBIT_PEER_GROUP;
+  constexpr int G = kPeerGroup;
   return 32 / (W * M) >= G ? G : (32 / (W * M) >= 1 ? 32 / (W * M) : 1);
 }
 
-// Loads of peers g .. g+G-1 (those below npeers) for the W slots of a trip.
-template <int IN_BITS, int BITS, int R, int W, int G, bool GUARD>
+// The number of peers: NPC when it is fixed at compile time (NPC > 0), else
+// the run-time count.  With a fixed count the peer loop is straight-line code:
+// the peers' pointers come from the kernel arguments in one batch of scalar
+// loads and all of the group's vector loads issue back to back.
+template <int NPC>
+__device__ __forceinline__ int peer_count(const ReduceArgs& a) {
+  return NPC > 0 ? NPC : a.npeers;
+}
+
+// Loads of peers g .. g+G-1 (those below the peer count) for the W slots of
+// a trip.  The pointers of all G peers are read first (the argument block
+// holds kMaxPeers entries and g + G <= kMaxPeers), so that their scalar loads
+// are not each waited for between the vector loads of two peers.
+template <int IN_BITS, int BITS, int R, int W, int G, bool GUARD, int NPC>
 __device__ __forceinline__ void load_peer_group(const ReduceArgs& a, int g, const int64_t* wt,
                                                 const int64_t* kt, const uint32_t* wl,
                                                 const uint32_t* kl, const bool* in,
                                                 uint32_t (*w)[W][in_words<IN_BITS, BITS>()],
                                                 uint32_t (*sc)[W]) {
   constexpr int M = in_words<IN_BITS, BITS>();
-  const int np = a.npeers;
+  static_assert(kMaxPeers % G == 0, "peer groups tile the argument block");
+  const int np = peer_count<NPC>(a);
   const int64_t nwin = (a.n * IN_BITS + 31) / 32;       // input words per peer
   (void)nwin;
+  const uint32_t* cps[G];
+  const uint16_t* sps[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    cps[q] = a.codes[g + q];
+    sps[q] = a.scales[g + q];
+  }
 #pragma unroll
   for (int q = 0; q < G; ++q) {
     if (g + q < np) {                                   // wave-uniform
-      const uint32_t* cp = a.codes[g + q];
-      const uint16_t* sp = a.scales[g + q];
+      const uint32_t* cp = cps[q];
+      const uint16_t* sp = sps[q];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
         if (GUARD) {
@@ -143,14 +160,14 @@ __device__ __forceinline__ void load_peer_group(const ReduceArgs& a, int g, cons
 
 // Decode loaded peers g .. g+G-1 into acc, in peer order (peer 0 starts the
 // sums).
-template <int IN_BITS, int BITS, int W, int G>
+template <int IN_BITS, int BITS, int W, int G, int NPC>
 __device__ __forceinline__ void decode_peer_group(const ReduceArgs& a, int g,
                                                   const uint32_t (*w)[W][in_words<IN_BITS, BITS>()],
                                                   const uint32_t (*sc)[W],
                                                   float (*acc)[Grid<BITS>::E]) {
   constexpr int M = in_words<IN_BITS, BITS>();
   constexpr int EIN = Grid<IN_BITS>::E;
-  const int np = a.npeers;
+  const int np = peer_count<NPC>(a);
 #pragma unroll
   for (int q = 0; q < G; ++q) {
     if (g + q < np) {
@@ -287,11 +304,11 @@ __device__ __forceinline__ void requant_tiles(
 
 // Reduce and requantize NT consecutive output tiles starting at tile `tile0`,
 // any number of peers (groups of G: all loads of a group are issued before
-// any of its peers is decoded).  GUARD: the tiles may reach past the end of
-// the buffer (only in the tail kernel): loads past the end read 0 and those
-// positions are +0 for the statistic.  EF: stage-2 error feedback with the
-// residual a.resid.
-template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD>
+// any of its peers is decoded; NPC > 0: exactly NPC peers).  GUARD: the tiles
+// may reach past the end of the buffer (only in the tail kernel): loads past
+// the end read 0 and those positions are +0 for the statistic.  EF: stage-2
+// error feedback with the residual a.resid.
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD, int NPC = 0>
 __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R, W = NT * R;
@@ -305,11 +322,20 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
   float e[NT][R][E];
   if constexpr (EF) load_residual<BITS, LOG2B, NT, GUARD>(a, tile0, e);
   float acc[NT][R][E];
+  if constexpr (NPC > 0) {
+#pragma unroll
+    for (int g = 0; g < NPC; g += G) {
+      uint32_t w[G][W][M], sc[G][W];
+      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, NPC>(a, g, wt, kt, wl, kl, in, w, sc);
+      decode_peer_group<IN_BITS, BITS, W, G, NPC>(a, g, w, sc, &acc[0][0]);
+    }
+  } else {
 #pragma unroll 1
-  for (int g = 0; g < a.npeers; g += G) {
-    uint32_t w[G][W][M], sc[G][W];
-    load_peer_group<IN_BITS, BITS, R, W, G, GUARD>(a, g, wt, kt, wl, kl, in, w, sc);
-    decode_peer_group<IN_BITS, BITS, W, G>(a, g, w, sc, &acc[0][0]);
+    for (int g = 0; g < a.npeers; g += G) {
+      uint32_t w[G][W][M], sc[G][W];
+      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, 0>(a, g, wt, kt, wl, kl, in, w, sc);
+      decode_peer_group<IN_BITS, BITS, W, G, 0>(a, g, w, sc, &acc[0][0]);
+    }
   }
   requant_tiles<IN_BITS, BITS, LOG2B, SR, EF, NT, GUARD>(a, tile0, acc, e);
 }
@@ -332,8 +358,18 @@ __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int
   } else {
     const int64_t ntrips = first / U;
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-    for (int64_t trip = global_wave_id(); trip < ntrips; trip += nwaves)
-      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false>(a, trip * U);
+    const int64_t trip = global_wave_id();
+    // eight peers (one per GPU of an 8-GPU node): the straight-line form.
+    // The grid gives every wave one trip; the loop only runs where the grid
+    // was capped (more than 2^32 work-items), so the first trip is kept out
+    // of it and its addresses are not carried from trip to trip.
+    if (a.npeers == 8) {
+      if (trip < ntrips) reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 8>(a, trip * U);
+    } else {
+      if (trip < ntrips) reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0>(a, trip * U);
+    }
+    for (int64_t t = trip + nwaves; t < ntrips; t += nwaves)
+      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0>(a, t * U);
   }
 }
 

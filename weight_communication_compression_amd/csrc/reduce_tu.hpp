@@ -15,29 +15,24 @@ namespace lowbit {
 // plain reduce keeps the general tile (40 -> 49 us in the row layout, where
 // two lanes load each code word and every lane its scale; at 2 bits
 // 33 -> 58 us).
-#ifndef LOWBIT_ROW_REDUCE_4
-#define LOWBIT_ROW_REDUCE_4 1
-#endif
 template <int BITS, int LOG2B, bool SR, bool EF>
 static lowbit_status launch_rr(const ReduceArgs& a, hipStream_t s) {
   using S = RowShape<BITS, LOG2B, EF ? kErrorFeedback : kPlain>;
   const int64_t full_trips = a.n / S::TILE;
-  if (full_trips > 0) {
-    hipLaunchKernelGGL((rowr_kernel<BITS, LOG2B, SR, EF, false>), dim3(grid_for_tiles(full_trips)),
-                       dim3(kBlockThreads), 0, s, a, full_trips);
-  }
-  if (full_trips * S::TILE < a.n) {
-    hipLaunchKernelGGL((rowr_kernel<BITS, LOG2B, SR, EF, true>), dim3(1), dim3(kWave), 0, s, a,
-                       full_trips);
-  }
-  return launch_status();
+  lowbit_status st = LOWBIT_OK;
+  if (full_trips > 0)
+    st = launch(&rowr_kernel<BITS, LOG2B, SR, EF, false>, grid_for_tiles(full_trips),
+                kBlockThreads, s, a, full_trips);
+  if (st == LOWBIT_OK && full_trips * S::TILE < a.n)
+    st = launch(&rowr_kernel<BITS, LOG2B, SR, EF, true>, 1, kWave, s, a, full_trips);
+  return st;
 }
 
 // Main kernel over the complete trips of full tiles; one-wave tail kernel for
 // whatever remains.
 template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF>
 static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
-  if constexpr (IN_BITS == BITS && BITS == 4 && LOWBIT_ROW_REDUCE_4) {
+  if constexpr (IN_BITS == BITS && BITS == 4) {
     if (EF || a.out_sum) return launch_rr<BITS, LOG2B, SR, EF>(a, s);
   }
   {
@@ -45,15 +40,13 @@ static lowbit_status launch_r(const ReduceArgs& a, hipStream_t s) {
     constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
     const int64_t full_tiles = a.n / S::TILE;
     const int64_t ntrips = full_tiles / U;
-    if (ntrips > 0) {
-      hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, false>),
-                         dim3(grid_for_tiles(ntrips)), dim3(kBlockThreads), 0, s, a, full_tiles);
-    }
-    if (ntrips * U * S::TILE < a.n) {
-      hipLaunchKernelGGL((reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, true>), dim3(1),
-                         dim3(kWave), 0, s, a, ntrips * U);
-    }
-    return launch_status();
+    lowbit_status st = LOWBIT_OK;
+    if (ntrips > 0)
+      st = launch(&reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, false>, grid_for_tiles(ntrips),
+                  kBlockThreads, s, a, full_tiles);
+    if (st == LOWBIT_OK && ntrips * U * S::TILE < a.n)
+      st = launch(&reduce_kernel<IN_BITS, BITS, LOG2B, SR, EF, true>, 1, kWave, s, a, ntrips * U);
+    return st;
   }
 }
 

@@ -16,7 +16,7 @@
 // compress, 64 Mi binary32: one coalesced row per wave 121.5 us, two rows
 // 125.6, the 32-byte lane stride of the general tile 130 us.)
 //
-// A trip is max(LOWBIT_ROW_ROWS[_EF], B/256) rows, so it holds whole blocks;
+// A trip is max(kRowRows or kRowRowsEf, B/256) rows, so it holds whole blocks;
 // the block statistic is the integer DPP maximum over the B/4 lanes of a
 // block within a row, then over the block's rows.  The arithmetic per element
 // is that of the general tile: v = x * fl(1/s); nearest: clamp, then round by
@@ -32,19 +32,15 @@ namespace lowbit {
 
 // rows of 256 per trip (at least one block), plain / weight-difference and
 // error-feedback / EF21 modes
-#ifndef LOWBIT_ROW_ROWS
-#define LOWBIT_ROW_ROWS 2
-#endif
-#ifndef LOWBIT_ROW_ROWS_EF
-#define LOWBIT_ROW_ROWS_EF 1
-#endif
+constexpr int kRowRows = 2;
+constexpr int kRowRowsEf = 1;
 
 template <int BITS, int LOG2B, int MODE>
 struct RowShape {
   static constexpr int B = 1 << LOG2B;
   static constexpr int ROW = kWave * 4;                  // elements per row
   static constexpr int RMIN =
-      (MODE == kErrorFeedback || MODE == kEF21) ? LOWBIT_ROW_ROWS_EF : LOWBIT_ROW_ROWS;
+      (MODE == kErrorFeedback || MODE == kEF21) ? kRowRowsEf : kRowRows;
   static constexpr int RT = B > RMIN * ROW ? B / ROW : RMIN;   // rows per trip
   static constexpr int TILE = ROW * RT;
   static constexpr int LB = B >= ROW ? kWave : B / 4;    // lanes of a block within a row
@@ -189,12 +185,12 @@ __global__ __launch_bounds__(kBlockThreads) void row_kernel(QuantArgs a, int64_t
     }
   } else {
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-    for (int64_t trip = global_wave_id(); trip < first; trip += nwaves) {
+    for_each_trip(global_wave_id(), first, nwaves, [&](int64_t trip) __attribute__((always_inline)) {
       const int64_t t0 = trip * S::TILE;
       float v[RT][4], h[RT][4];
       row_load<RT, DT, MODE, true>(a, t0, v, h);
       row_finish<BITS, LOG2B, SR, MODE, true>(a, t0, v, h);
-    }
+    });
   }
 }
 

@@ -36,28 +36,56 @@ __device__ __forceinline__ void accumulate_piece(uint32_t piece, float s, float*
   }
 }
 
-template <int BITS, int LOG2B, bool SR, bool EF, bool FULL>
+// Workgroups per XCD run (logical_block): a 128-byte line of one peer's
+// scales serves 8 workgroups of this kernel.
+#ifndef LOWBIT_ROWR_XCD_CHUNK
+#define LOWBIT_ROWR_XCD_CHUNK 8
+#endif
+constexpr int kRowrXcdChunk = LOWBIT_ROWR_XCD_CHUNK;
+
+template <int BITS, int LOG2B, bool SR, bool EF, bool FULL, int NPC = 0>
 __device__ __forceinline__ void rowr_trip(const ReduceArgs& a, int64_t t0) {
   constexpr int MODE = EF ? kErrorFeedback : kPlain;
   using S = RowShape<BITS, LOG2B, MODE>;
-  constexpr int RT = S::RT, E = Grid<BITS>::E, G = 8;
+  // peers whose loads are in flight together: 8, fewer for trips of more
+  // than two rows, so that a lane holds at most 16 code words and 16 scales
+  constexpr int RT = S::RT, E = Grid<BITS>::E, G = RT <= 2 ? 8 : (16 / RT > 1 ? 16 / RT : 1);
   constexpr float UNSCALE = 1.0f / (float)(1 << acc_shift<BITS>());   // exact
   const int lane = lane_id();
   const int lbi = a.in_log2b;
-  const int np = a.npeers;
+  const int np = peer_count<NPC>(a);
   const int64_t n = a.n;
   const uint32_t lo = 4u * (uint32_t)lane;
   const int sh = (int)(lo % E) * BITS;                      // the lane's piece in its word
 
   float acc[RT][4];
-#pragma unroll 1
+  // the stage-2 residual, loaded with the first peers (positions past the
+  // end read 0)
+  float e[RT][4];
+  if constexpr (EF) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint32_t off = (uint32_t)(r * S::ROW) + lo;
+      if (FULL) load_vec<kF32, 4>(a.resid, t0, off, e[r]);
+      else load_tail<kF32, 4>(a.resid, t0, off, n - t0, e[r]);
+    }
+  }
+  static_assert(kMaxPeers % G == 0, "peer groups tile the argument block");
+#pragma unroll(NPC > 0 ? 16 : 1)
   for (int g = 0; g < np; g += G) {
     uint32_t w[G][RT], sc[G][RT];
+    const uint32_t* cps[G];
+    const uint16_t* sps[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      cps[q] = a.codes[g + q];
+      sps[q] = a.scales[g + q];
+    }
 #pragma unroll
     for (int q = 0; q < G; ++q) {
       if (g + q < np) {                                     // wave-uniform
-        const uint32_t* cp = a.codes[g + q];
-        const uint16_t* sp = a.scales[g + q];
+        const uint32_t* cp = cps[q];
+        const uint16_t* sp = sps[q];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           const int64_t i0 = t0 + r * S::ROW + lo;
@@ -101,16 +129,11 @@ __device__ __forceinline__ void rowr_trip(const ReduceArgs& a, int64_t t0) {
     }
   }
   if constexpr (EF) {
-    // a = fl(sum + e); the residual past the end reads 0
+    // a = fl(sum + e)
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const uint32_t off = (uint32_t)(r * S::ROW) + lo;
-      float e[4];
-      if (FULL) load_vec<kF32, 4>(a.resid, t0, off, e);
-      else load_tail<kF32, 4>(a.resid, t0, off, n - t0, e);
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[r][j] = v[r][j] + e[j];
-    }
+      for (int j = 0; j < 4; ++j) v[r][j] = v[r][j] + e[r][j];
   }
   QuantArgs qa{};
   qa.n = n;
@@ -136,8 +159,16 @@ __global__ __launch_bounds__(kBlockThreads) void rowr_kernel(ReduceArgs a, int64
     }
   } else {
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-    for (int64_t trip = global_wave_id(); trip < first; trip += nwaves)
-      rowr_trip<BITS, LOG2B, SR, EF, true>(a, trip * S::TILE);
+    const int64_t trip = global_wave_id<kBlockThreads, kRowrXcdChunk>();
+    // eight peers (one per GPU of an 8-GPU node): the straight-line form.
+    // The first trip is kept out of the loop (see for_each_trip), which only
+    // runs where the grid was capped.
+    if (trip < first) {
+      if (a.npeers == 8) rowr_trip<BITS, LOG2B, SR, EF, true, 8>(a, trip * S::TILE);
+      else rowr_trip<BITS, LOG2B, SR, EF, true, 0>(a, trip * S::TILE);
+    }
+    for (int64_t t = trip + nwaves; t < first; t += nwaves)
+      rowr_trip<BITS, LOG2B, SR, EF, true, 0>(a, t * S::TILE);
   }
 }
 

@@ -42,7 +42,7 @@ struct SignShape {
 // Load RT rows of 256 elements from element t0, four consecutive elements
 // per lane and row (plus the residual, minus the old weights, or minus the
 // EF21 state, as in the general compress); positions at or past n read +0.
-template <int RT, int DT, int MODE, bool FULL>
+template <int RT, int DT, int MODE, bool FULL, bool NTX = false>
 __device__ __forceinline__ void row_load(const QuantArgs& a, int64_t t0, float (&v)[RT][4],
                                          float (&h)[RT][4]) {
   const int lane = lane_id();
@@ -52,9 +52,8 @@ __device__ __forceinline__ void row_load(const QuantArgs& a, int64_t t0, float (
     float w[4];
     if constexpr (FULL) {
       constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
-      load_vec<DT, 4, (MODE == kPlain && LOWBIT_X_NT_LOADS) || (RMW && LOWBIT_EF_NT_LOADS >= 2)>(
-          a.x, t0, off, v[r]);
-      if constexpr (RMW) load_vec<kF32, 4, LOWBIT_EF_NT_LOADS >= 1>(a.resid, t0, off, w);
+      load_vec<DT, 4, NTX && stream_capable<MODE, DT, 4>()>(a.x, t0, off, v[r]);
+      if constexpr (RMW) load_vec<kF32, 4>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, 4>(a.x2, t0, off, w);
     } else {
       load_tail<DT, 4>(a.x, t0, off, a.n - t0, v[r]);
@@ -174,7 +173,8 @@ __device__ __forceinline__ void sign_finish(const QuantArgs& a, int64_t t0,
 // Main kernel (TAIL = false): one full tile per wave, no bounds checks; the
 // grid covers the `first` full tiles.  Tail kernel (TAIL = true, one wave):
 // the remaining tiles from tile `first`, the last of which may be partial.
-template <int LOG2B, int DT, int MODE, bool TAIL>
+// NTX: read x with non-temporal loads where stream_capable.
+template <int LOG2B, int DT, int MODE, bool TAIL, bool NTX = false>
 __global__ __launch_bounds__(kBlockThreads) void sign_kernel(QuantArgs a, int64_t first) {
   using S = SignShape<LOG2B>;
   constexpr int RT = S::RT;
@@ -194,12 +194,12 @@ __global__ __launch_bounds__(kBlockThreads) void sign_kernel(QuantArgs a, int64_
     }
   } else {
     const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-    for (int64_t tile = global_wave_id(); tile < first; tile += nwaves) {
+    for_each_trip(global_wave_id(), first, nwaves, [&](int64_t tile) __attribute__((always_inline)) {
       const int64_t t0 = tile * S::TILE;
       float v[RT][4], h[RT][4];
-      row_load<RT, DT, MODE, true>(a, t0, v, h);
+      row_load<RT, DT, MODE, true, NTX>(a, t0, v, h);
       sign_finish<LOG2B, MODE, true>(a, t0, v, h);
-    }
+    });
   }
 }
 

@@ -21,11 +21,12 @@ __all__ = [
     "LowbitError", "lib", "library_path", "num_words", "num_blocks", "QParams",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
     "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams", "add_inplace_f32", "fold_f32",
-    "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16",
+    "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16", "HINT_INPUT_REUSED",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
+HINT_INPUT_REUSED = 1        # lowbit_qparams.hints: the input is read again soon
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "liblowbit.so")
@@ -42,7 +43,7 @@ class LowbitError(RuntimeError):
 class QParams(ctypes.Structure):
     """lowbit_qparams"""
     _fields_ = [("bitwidth", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("stochastic", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stochastic", ctypes.c_int32), ("hints", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("index_offset", ctypes.c_uint64)]
 
 
@@ -121,8 +122,8 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _qp(bitwidth, block_size, stochastic=False, seed=0, index_offset=0) -> QParams:
-    return QParams(int(bitwidth), int(block_size), int(bool(stochastic)), 0,
+def _qp(bitwidth, block_size, stochastic=False, seed=0, index_offset=0, hints=0) -> QParams:
+    return QParams(int(bitwidth), int(block_size), int(bool(stochastic)), int(hints),
                    int(seed) & (2 ** 64 - 1), int(index_offset))
 
 
@@ -159,12 +160,16 @@ def _out_scales(n, block_size, like, scales):
 # -------------------------------------------------------------- the codec --
 def quantize_pack(x: torch.Tensor, bitwidth: int, block_size: int, stochastic: bool = False,
                   seed: int = 0, index_offset: int = 0, codes: Optional[torch.Tensor] = None,
-                  scales: Optional[torch.Tensor] = None):
-    """Compress x (float32 or bfloat16) -> (codes int32[num_words], scales float16[num_blocks])."""
+                  scales: Optional[torch.Tensor] = None, input_reused: bool = False):
+    """Compress x (float32 or bfloat16) -> (codes int32[num_words], scales float16[num_blocks]).
+
+    input_reused: the caller reads x again soon (LOWBIT_HINT_INPUT_REUSED), so
+    it is kept in the caches rather than streamed."""
     n = x.numel()
     codes = _out_codes(n, bitwidth, x, codes)
     scales = _out_scales(n, block_size, x, scales)
-    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset)
+    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset,
+             HINT_INPUT_REUSED if input_reused else 0)
     _check(lib().lowbit_quantize_pack(_dev(x, "x"), _dtype_code(x), n, ctypes.byref(qp),
                                       _dev(codes, "codes"), _dev(scales, "scales"), _stream(x)),
            "lowbit_quantize_pack")
