@@ -192,6 +192,19 @@ def main() -> int:
     keep = []        # keep ctypes objects alive
     results = {}     # the step's output buffers, checked against the oracle at the end
 
+    nw, nb = L.num_words(N, EF_BITS), L.num_blocks(N, BLOCK)
+    ec = torch.empty(nw, dtype=torch.int32, device=dev)
+    es = torch.empty(nb, dtype=torch.float16, device=dev)
+    qe = qp(EF_BITS, BLOCK, True, SEED, 0)
+    keep += [ec, es, qe]
+    a = (P(x.data_ptr()), L.F32, P(resid.data_ptr()), N, ctypes.byref(qe), P(ec.data_ptr()),
+         P(es.data_ptr()))
+    # the EF compress first, as in the timed schedule (it runs alone at the
+    # start of each step); the kernel after it pays for the residual lines it
+    # leaves dirty in the Infinity Cache
+    stages.append((f"ef_compress b{EF_BITS}", kname_quant(EF_BITS, 8, True, 0, 1),
+                   3 * N * 4 + nw * 4 + nb * 2, (lib.lowbit_ef_compress, a)))
+
     for b in BITS:
         nw, nb = L.num_words(N, b), L.num_blocks(N, BLOCK)
         codes = torch.empty(nw, dtype=torch.int32, device=dev)
@@ -224,16 +237,6 @@ def main() -> int:
         a = (P(codes.data_ptr()), P(scales.data_ptr()), N, ctypes.byref(qd), P(yb.data_ptr()))
         stages.append((f"unpack_dequant b{b}", kname_dequant(b, 0, 0),
                        nw * 4 + nb * 2 + N * 4, (lib.lowbit_unpack_dequant, a)))
-
-    nw, nb = L.num_words(N, EF_BITS), L.num_blocks(N, BLOCK)
-    ec = torch.empty(nw, dtype=torch.int32, device=dev)
-    es = torch.empty(nb, dtype=torch.float16, device=dev)
-    qe = qp(EF_BITS, BLOCK, True, SEED, 0)
-    keep += [ec, es, qe]
-    a = (P(x.data_ptr()), L.F32, P(resid.data_ptr()), N, ctypes.byref(qe), P(ec.data_ptr()),
-         P(es.data_ptr()))
-    stages.append((f"ef_compress b{EF_BITS}", kname_quant(EF_BITS, 8, True, 0, 1),
-                   3 * N * 4 + nw * 4 + nb * 2, (lib.lowbit_ef_compress, a)))
 
     nw, nb = L.num_words(N, W_BITS), L.num_blocks(N, W_BLOCK)
     wc = torch.empty(nw, dtype=torch.int32, device=dev)
@@ -680,35 +683,58 @@ def measure_configs(L, dev, reps=20):
           lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s), n * 2)
     del g, e, c, s
 
-    # local reduce of 8 peer chunks of 32 Mi, b4 B128 in and out
+    # local reduce of 8 peer chunks of 32 Mi, b4 B128 in and out, with the
+    # peers in two placements: separately allocated buffers, and the layout an
+    # all-to-all exchange delivers (one receive buffer holding each peer's
+    # message -- its codes, then its scales -- back to back)
     n = 32 << 20
-    pc, ps = [], []
-    for _ in range(8):
+    nw4, nb4 = L.num_words(n, 4), L.num_blocks(n, 128)
+    msg = nw4 * 4 + nb4 * 2                          # bytes of one peer's message
+    recv = torch.empty(8 * msg // 4, dtype=torch.int32, device=dev)
+    layouts = {
+        "": ([torch.empty(nw4, dtype=torch.int32, device=dev) for _ in range(8)],
+             [torch.empty(nb4, dtype=torch.float16, device=dev) for _ in range(8)]),
+        ", receive buffer": ([recv[p * msg // 4: p * msg // 4 + nw4] for p in range(8)],
+                             [recv[(p * msg + nw4 * 4) // 4:(p * msg + nw4 * 4 + nb4 * 2) // 4]
+                              .view(torch.float16) for p in range(8)])}
+    for p in range(8):
         xp = torch.randn(n, device=dev, generator=gen)
-        a, b = L.quantize_pack(xp, 4, 128)
-        pc.append(a)
-        ps.append(b)
+        for pc, ps in layouts.values():
+            L.quantize_pack(xp, 4, 128, codes=pc[p], scales=ps[p])
         del xp
-    oc = torch.empty(L.num_words(n, 4), dtype=torch.int32, device=dev)
-    os_ = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
-    timed("reduce_requant 8x32Mi", f"8 x {n} peers, b4 B128 -> b4 B128 nearest",
-          9 * (oc.numel() * 4 + os_.numel() * 2),
-          lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_), 8 * n * 4)
+    oc = torch.empty(nw4, dtype=torch.int32, device=dev)
+    os_ = torch.empty(nb4, dtype=torch.float16, device=dev)
     tot = torch.empty(n, dtype=torch.float32, device=dev)
-    timed("reduce_requant 8x32Mi +sum", f"8 x {n} peers, b4 B128 -> b4 B128 nearest, "
-          "fp32 sum written", 9 * (oc.numel() * 4 + os_.numel() * 2) + n * 4,
-          lambda: L.reduce_requant(pc, ps, n, 4, 128, want_sum=True, out_codes=oc,
-                                   out_scales=os_, out_sum=tot), 8 * n * 4)
-    # bandwidth reference for that access pattern: XOR of the 8 peers' code
-    # streams read the way the reduce reads them, one output stream, no
-    # arithmetic
-    timed("xor_streams 8x16MiB reference", f"XOR of the 8 peers' code streams "
-          f"({oc.numel()} words each) with the reduce's access pattern; not a codec step",
-          9 * oc.numel() * 4, lambda: L.xor_streams(pc, oc), 8 * n * 4)
-    ref = out["xor_streams 8x16MiB reference"]["alg_GBps"]
-    for k in ("reduce_requant 8x32Mi", "reduce_requant 8x32Mi +sum"):
-        out[k]["of_pattern_reference"] = round(out[k]["alg_GBps"] / ref, 3)
-    del pc, ps, oc, os_, tot
+    for lay, (pc, ps) in layouts.items():
+        where = "separate buffers" if not lay else "one receive buffer, messages of codes + scales"
+        timed(f"reduce_requant 8x32Mi{lay}", f"8 x {n} peers ({where}), b4 B128 -> b4 B128 "
+              "nearest", 9 * (nw4 * 4 + nb4 * 2),
+              lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_), 8 * n * 4)
+        timed(f"reduce_requant 8x32Mi +sum{lay}", f"8 x {n} peers ({where}), b4 B128 -> b4 B128 "
+              "nearest, fp32 sum written", 9 * (nw4 * 4 + nb4 * 2) + n * 4,
+              lambda: L.reduce_requant(pc, ps, n, 4, 128, want_sum=True, out_codes=oc,
+                                       out_scales=os_, out_sum=tot), 8 * n * 4)
+        # bandwidth reference for that access pattern: XOR of the 8 peers' code
+        # streams read the way the reduce reads them, one output stream, no
+        # arithmetic
+        timed(f"xor_streams 8x16MiB reference{lay}", f"XOR of the 8 peers' code streams "
+              f"({nw4} words each, {where}) with the reduce's access pattern; not a codec step",
+              9 * nw4 * 4, lambda: L.xor_streams(pc, oc), 8 * n * 4)
+        ref = out[f"xor_streams 8x16MiB reference{lay}"]["alg_GBps"]
+        for k in (f"reduce_requant 8x32Mi{lay}", f"reduce_requant 8x32Mi +sum{lay}"):
+            out[k]["of_pattern_reference"] = round(out[k]["alg_GBps"] / ref, 3)
+    # the same bytes as one stream: a 128 MiB read and a 16 MiB write (the
+    # compress-volume reference at 4 bits over 32 Mi binary32 values), against
+    # which the eight equally long streams read at once are compared
+    one = recv[:8 * nw4].view(torch.float32)
+    timed("fold 128MiB one-stream reference", "one contiguous 128 MiB read, 16 MiB written "
+          "(compress-volume reference kernel); not a codec step", 9 * nw4 * 4,
+          lambda: L.fold_f32(one, 4, oc), 8 * n * 4)
+    one_gbps = out["fold 128MiB one-stream reference"]["alg_GBps"]
+    for lay in layouts:
+        k = f"xor_streams 8x16MiB reference{lay}"
+        out[k]["of_one_stream"] = round(out[k]["alg_GBps"] / one_gbps, 3)
+    del layouts, recv, oc, os_, tot, one
 
     # weight difference on an 840 Mi bfloat16 shard, b4 B64
     n = 840 << 20
