@@ -152,6 +152,69 @@ def test_reduce_requant(bits, B, sr, P, want_sum):
         assert_same(f32_np(tot), wt, "sum")
 
 
+def _controlled_peer(kind, bits, B, n, p, seed):
+    """One peer's binary32 input whose blocks have an exactly chosen max |x|
+    of 2^e (so the block scales' binary16 exponents differ across peers by
+    the spread of e): 'limit' spreads e over 2^D (the widest the integer path
+    of the 8-peer reduce takes: D = 5 at 4 bits, 3 at 8 bits), 'over' one
+    step wider in one block in 40 (some waves take the integer path, others
+    the binary32 one), 'subnormal' and 'mixed' reach binary16-
+    subnormal scales, 'zeros' zeroes whole blocks of some peers (and some
+    blocks of all peers)."""
+    g = np.random.default_rng(seed)
+    nb = -(-n // B)
+    D = 5 if bits == 4 else 3
+    e = {"normal": np.zeros(nb, np.int64),
+         "limit": g.integers(0, D + 1, nb),
+         "over": g.integers(0, D + 1, nb),
+         "subnormal": g.integers(-24, -19, nb),
+         "mixed": g.integers(-15, -15 + D + 1, nb),
+         "zeros": g.integers(0, D + 1, nb)}[kind]
+    bg = np.random.default_rng(seed // 100)          # the same for every peer
+    if kind == "limit":
+        e[::7] = D if p % 2 else 0                    # some blocks exactly at the limit
+    if kind == "over":
+        e[::40] = D + 1 if p == 3 else 0              # some blocks one past it
+    x = g.uniform(-1.0, 1.0, n) * np.repeat(2.0 ** e, B)[:n]
+    starts = np.arange(0, n, B)
+    x[starts] = 2.0 ** e * np.where(g.random(nb) < 0.5, 1.0, -1.0)
+    if kind == "zeros":
+        zb = g.random(nb) < 0.3
+        zb[bg.random(nb) < 0.2] = True                # zero in every peer
+        for b in np.nonzero(zb)[0]:
+            x[b * B:(b + 1) * B] = 0.0
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "limit", "over", "subnormal", "mixed", "zeros"])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("B", [32, 64, 128, 256, 1024, 4096])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_reduce_eight_peers_exact_sums(bits, B, sr, kind):
+    """Eight peers (one per GPU of a node) whose block scales lie within or
+    just outside the range in which the reduce forms the peer-ordered sums in
+    integers: bit-identical to the oracle's binary32 sums either way, with and
+    without the sum output, over several waves and a ragged tail."""
+    n = 9 * _tile(bits, B) + B + 45
+    pcs, pss, gc, gs = [], [], [], []
+    for p in range(8):
+        x = _controlled_peer(kind, bits, B, n, p, 100 * (bits * B) + p)
+        c, s = O.quantize_pack(x, bits, B)
+        pcs.append(c)
+        pss.append(s)
+        gc.append(torch.from_numpy(c.view(np.int32)).cuda())
+        gs.append(torch.from_numpy(s.view(np.float16)).cuda())
+    say(f"reduce 8 peers bits={bits} B={B} sr={sr} kind={kind} n={n}")
+    wc, ws, wt = O.reduce_requant(pcs, pss, n, bits, B, bits, sr, 3, 0, want_sum=True)
+    for want_sum in (False, True):
+        c, s, tot = L.reduce_requant(gc, gs, n, bits, B, sr, 3, 0, want_sum=want_sum)
+        torch.cuda.synchronize()
+        assert_same(scales_np(s), ws, "scales")
+        assert_same(codes_np(c), wc, "codes")
+        if want_sum:
+            assert_same(f32_np(tot), wt, "sum")
+
+
 # -------------------------------------------------------- weight difference --
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B", [32, 64, 128, 2048])

@@ -18,8 +18,11 @@
 
 namespace lowbit {
 
-// output elements per lane per trip (8, 16 or 32 measured within noise)
-constexpr int kReduceElemsPerTrip = 16;
+// output elements per lane per trip.  Measured on 8 x 32 Mi peers, b4 B128,
+// with the integer sums: 8 elements (44 VGPRs, 8 waves per SIMD) 36.0 us
+// with separately allocated peers and 35.2 us in one receive buffer; 16
+// elements (84 VGPRs) 39.2 and 34.3 us.  8 is the steadier of the two.
+constexpr int kReduceElemsPerTrip = 8;
 
 template <int PER_LANE>
 constexpr int reduce_tiles_per_trip() {
@@ -302,6 +305,163 @@ __device__ __forceinline__ void requant_tiles(
   (void)e;
 }
 
+// ------------------------------------------------------------ exact sums --
+// Eight peers of 4- or 8-bit codes whose block scales lie within a factor
+// 2^D of each other (D = 5 at 4 bits, 3 at 8 bits): the peer-ordered binary32
+// sum then never rounds.  With u = 2^(Emin - 25) the unit of the smallest
+// nonzero scale (Emin its binary16 exponent field, 1 for a subnormal), every
+// scale is s_p = M_p * u with M_p = significand * 2^(E_p - Emin) an integer
+// below 2^16, every term q_p * s_p is an integer multiple of u, and every
+// partial sum is at most qmax * sum_p M_p < 2^24 units in magnitude, so each
+// binary32 addition is exact and the sum is S * u, S = sum_p q_p * M_p.  S is
+// formed exactly in 32-bit integers, two peers per v_dot2_u32_u16 on the
+// offset codes (S = sum_p c_p * M_p - 2^(b-1) * sum_p M_p), and float(S) * u
+// (both exact) is bit-identical to the rounded peer-ordered sum.  A wave in
+// which any block misses the condition takes the binary32 path.
+template <int BITS>
+constexpr uint32_t exact_spread() { return BITS == 4 ? 5u : 3u; }
+
+template <int IN_BITS, int BITS, int LOG2B, int NPC>
+constexpr bool exact_path() {
+  return NPC == 8 && IN_BITS == BITS && (BITS == 4 || BITS == 8) &&
+         TileShape<BITS, LOG2B>::L >= 8;
+}
+
+// Reductions of unsigned values over aligned groups of 8 lanes (every lane of
+// a group ends with the result), and the value of lane Q of the lane's group.
+__device__ __forceinline__ uint32_t group8_min(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = min(v, dpp_u32<0x4E>(v));     // quad_perm [2,3,0,1]
+  return min(v, dpp_u32<0x141>(v)); // row_half_mirror: the other quad
+}
+__device__ __forceinline__ uint32_t group8_max(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  return max(v, dpp_u32<0x141>(v));
+}
+__device__ __forceinline__ uint32_t group8_add(uint32_t v) {
+  v += dpp_u32<0xB1>(v);
+  v += dpp_u32<0x4E>(v);
+  return v + dpp_u32<0x141>(v);
+}
+template <int Q>
+__device__ __forceinline__ uint32_t group8_lane(uint32_t v) {
+  // ds_swizzle bit mode: lane (id & 0x18) | Q within each 32 lanes
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x18 | (Q << 5));
+}
+
+// 2^x as a binary32 value (x a normal exponent)
+__device__ __forceinline__ float pow2_f32(int x) { return __uint_as_float((uint32_t)(x + 127) << 23); }
+
+// Loads and peer sums of one trip of NT full tiles for exactly eight peers
+// (exact_path): acc as decode_peer_group leaves it, i.e. 2^acc_shift<BITS>()
+// times the peer-ordered binary32 sums.
+template <int BITS, int LOG2B, int NT>
+__device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t* wt,
+                                             const int64_t* kt, const uint32_t* wl,
+                                             const uint32_t* kl, float (*acc)[Grid<BITS>::E]) {
+  using S = TileShape<BITS, LOG2B>;
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  constexpr int E = S::E, R = S::R, W = NT * R;
+  constexpr int K = acc_shift<BITS>();
+  constexpr uint32_t HALF = Grid<BITS>::HALF;
+  const int p = lane_id() & 7;        // the peer whose scale this lane loads
+  // the code words of all eight peers (pointers read in one batch)
+  const uint32_t* cps[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) cps[q] = a.codes[q];
+  uint32_t w[8][W][1];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[q][i][0] = (cps[q] + wt[i / R])[wl[i]];
+  // one scale per lane and slot: peer p's scale of the lane's block (a block
+  // spans at least 8 lanes, so each aligned group of 8 lanes holds all eight)
+  const uint16_t* s01 = (p & 1) ? a.scales[1] : a.scales[0];
+  const uint16_t* s23 = (p & 1) ? a.scales[3] : a.scales[2];
+  const uint16_t* s45 = (p & 1) ? a.scales[5] : a.scales[4];
+  const uint16_t* s67 = (p & 1) ? a.scales[7] : a.scales[6];
+  const uint16_t* s03 = (p & 2) ? s23 : s01;
+  const uint16_t* s47 = (p & 2) ? s67 : s45;
+  const uint16_t* sp = (p & 4) ? s47 : s03;
+  uint32_t s16[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) s16[i] = (sp + kt[i / R])[kl[i]];
+  // per slot: exponent range of the group's nonzero scales
+  uint32_t lo[W];
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t e = (s16[i] >> 10) & 31u;
+    const uint32_t ep = e != 0 ? e : 1u;
+    const bool nz = s16[i] != 0;
+    lo[i] = group8_min(nz ? ep : 31u);
+    const uint32_t hi = group8_max(nz ? ep : 0u);
+    ok = ok && (hi == 0 || hi <= lo[i] + exact_spread<BITS>());
+  }
+  if (__all(ok)) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const uint32_t e = (s16[i] >> 10) & 31u;
+      const uint32_t ep = e != 0 ? e : 1u;
+      const uint32_t m = (s16[i] & 0x3FFu) | (e != 0 ? 0x400u : 0u);
+      const uint32_t M = s16[i] != 0 ? m << (ep - lo[i]) : 0u;    // < 2^16
+      const uint32_t sumM = group8_add(M);
+      const uint32_t pair = M | (dpp_u32<0xB1>(M) << 16);          // peers p, p ^ 1
+      const u16x2 mp[4] = {__builtin_bit_cast(u16x2, group8_lane<0>(pair)),
+                           __builtin_bit_cast(u16x2, group8_lane<2>(pair)),
+                           __builtin_bit_cast(u16x2, group8_lane<4>(pair)),
+                           __builtin_bit_cast(u16x2, group8_lane<6>(pair))};
+      uint32_t sum[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        // 4 bits: odd elements are the high nibbles of bytes, summed 16x
+        const uint32_t f = (BITS == 4 && (j & 1)) ? 16u : 1u;
+        sum[j] = 0u - HALF * f * sumM;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t we = w[2 * j][i][0], wo = w[2 * j + 1][i][0];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // bytes k of the two peers' words in the two 16-bit halves
+          const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
+          const uint32_t b2 = __builtin_amdgcn_perm(wo, we, sel);
+          if constexpr (BITS == 4) {
+            sum[2 * k] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2 & 0x000F000Fu), mp[j],
+                                                sum[2 * k], false);
+            sum[2 * k + 1] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2 & 0x00F000F0u),
+                                                    mp[j], sum[2 * k + 1], false);
+          } else {
+            sum[k] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2), mp[j], sum[k], false);
+          }
+        }
+      }
+      // binary32 sums, scaled like the binary32 path's: 2^K * S * u
+      const int x = (int)(lo[i] < 30u ? lo[i] : 30u) - 25 + K;
+      const float unit = pow2_f32(x), unit16 = pow2_f32(x - 4);
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        acc[i][j] = (float)(int)sum[j] * ((BITS == 4 && (j & 1)) ? unit16 : unit);
+    }
+  } else {
+    // the binary32 path, with every peer's scale from the lane's group
+    uint32_t sc[8][W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      sc[0][i] = group8_lane<0>(s16[i]);
+      sc[1][i] = group8_lane<1>(s16[i]);
+      sc[2][i] = group8_lane<2>(s16[i]);
+      sc[3][i] = group8_lane<3>(s16[i]);
+      sc[4][i] = group8_lane<4>(s16[i]);
+      sc[5][i] = group8_lane<5>(s16[i]);
+      sc[6][i] = group8_lane<6>(s16[i]);
+      sc[7][i] = group8_lane<7>(s16[i]);
+    }
+    decode_peer_group<BITS, BITS, W, 8, 8>(a, 0, w, sc, acc);
+  }
+}
+
 // Reduce and requantize NT consecutive output tiles starting at tile `tile0`,
 // any number of peers (groups of G: all loads of a group are issued before
 // any of its peers is decoded; NPC > 0: exactly NPC peers).  GUARD: the tiles
@@ -322,7 +482,9 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
   float e[NT][R][E];
   if constexpr (EF) load_residual<BITS, LOG2B, NT, GUARD>(a, tile0, e);
   float acc[NT][R][E];
-  if constexpr (NPC > 0) {
+  if constexpr (!GUARD && exact_path<IN_BITS, BITS, LOG2B, NPC>()) {
+    reduce8_sums<BITS, LOG2B, NT>(a, wt, kt, wl, kl, &acc[0][0]);
+  } else if constexpr (NPC > 0) {
 #pragma unroll
     for (int g = 0; g < NPC; g += G) {
       uint32_t w[G][W][M], sc[G][W];
