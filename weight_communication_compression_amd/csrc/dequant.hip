@@ -10,8 +10,8 @@ static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
   constexpr int ROW = kWave * dequant_epl<APPLY>();
   const int64_t nrows = (a.n + ROW - 1) / ROW;
   const int64_t ntrips = (nrows + ROWS - 1) / ROWS;
-  return launch(&dequant_kernel<BITS, APPLY, DT>, grid_for_tiles<kDeqThreads>(ntrips), kDeqThreads,
-                s, a);
+  constexpr int THREADS = deq_threads<BITS, APPLY>();
+  return launch(&dequant_kernel<BITS, APPLY, DT>, grid_for_tiles<THREADS>(ntrips), THREADS, s, a);
 }
 
 template <int BITS>

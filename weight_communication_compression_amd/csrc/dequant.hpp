@@ -144,13 +144,18 @@ __device__ __forceinline__ void dequant_trip(const DequantArgs& a, int64_t base)
 // EPL*l .. EPL*l + EPL - 1 (their codes are EPL*b consecutive bits of one
 // word, or two words for 8 codes of 8 bits); blocks are >= 32 elements, so
 // each lane needs one scale.
+// workgroup size of the decompress / apply of BITS-bit codes
+template <int BITS, int APPLY>
+constexpr int deq_threads() { return kDeqThreads; }
+
 template <int BITS, int APPLY, int DT>
-__global__ __launch_bounds__(kDeqThreads) void dequant_kernel(DequantArgs a) {
+__global__ __launch_bounds__((deq_threads<BITS, APPLY>())) void dequant_kernel(DequantArgs a) {
+  constexpr int THREADS = deq_threads<BITS, APPLY>();
   constexpr int kDequantRows = dequant_rows<APPLY>();
   constexpr int ROW = kWave * dequant_epl<APPLY>();
   static_assert(ROW == 256 || ROW == 512, "rows of 256 or 512 elements");
-  const int64_t wave = global_wave_id<kDeqThreads>();
-  const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
+  const int64_t wave = global_wave_id<THREADS>();
+  const int64_t nwaves = (int64_t)gridDim.x * (THREADS / kWave);
   const int64_t nrows = (a.n + ROW - 1) / ROW;
   const int64_t ntrips = (nrows + kDequantRows - 1) / kDequantRows;
   for_each_trip(wave, ntrips, nwaves, [&](int64_t t) __attribute__((always_inline)) {

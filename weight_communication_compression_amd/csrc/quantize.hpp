@@ -166,6 +166,45 @@ __device__ __forceinline__ void quantize_tile(
   }
 }
 
+// The plain compress of binary32 input with more than four elements per lane
+// (2 and 4 bits: a lane's word spans 64 or 32 bytes, so each 16-byte load
+// instruction of a wave would touch half lines that the next one fetches
+// again) reads its tile through LDS: the wave loads the tile with coalesced
+// 16-byte loads (lane l takes bytes 16 * (64 k + l) of the tile, each
+// instruction one contiguous kilobyte) -- non-temporal when streamed --,
+// writes them to its own LDS slice and reads back its E consecutive elements.
+// A wave's LDS accesses execute in order, so no barrier is needed; the wave
+// barrier keeps the compiler from moving the reads above the writes.  (One
+// tile per trip whenever E > 4 for this mode, so one slice per wave.)
+template <int MODE, int DT, int E, int R>
+constexpr bool staged_tile() {
+  return MODE == kPlain && DT == kF32 && E > 4 && R == 1;
+}
+
+template <int E, bool NT>
+__device__ __forceinline__ void load_tile_staged(const float* x, int64_t t0, float* v) {
+  constexpr int Q = E / 4;                               // 16-byte pieces per lane
+  __shared__ f32x4 stage[kBlockThreads / kWave][kWave * Q];
+  f32x4* st = stage[threadIdx.x >> 6];
+  const int lane = lane_id();
+  const f32x4* src = reinterpret_cast<const f32x4*>(x + t0);
+  f32x4 t[Q];
+#pragma unroll
+  for (int k = 0; k < Q; ++k)
+    t[k] = NT ? __builtin_nontemporal_load(src + k * kWave + lane) : src[k * kWave + lane];
+#pragma unroll
+  for (int k = 0; k < Q; ++k) st[k * kWave + lane] = t[k];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    const f32x4 u = st[lane * Q + j];
+    v[4 * j + 0] = u.x;
+    v[4 * j + 1] = u.y;
+    v[4 * j + 2] = u.z;
+    v[4 * j + 3] = u.w;
+  }
+}
+
 // Load one tile's values (x, plus the residual or minus the old weights or
 // minus the EF21 state).  EF21 keeps the state in `h` for finish_tile.
 template <int BITS, int LOG2B, int DT, int MODE, bool FULL, bool NTX = false>
@@ -179,9 +218,11 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
   for (int r = 0; r < R; ++r) {
     const uint32_t off = (uint32_t)(r * kWave + lane) * E;
     float w[E];
-    if constexpr (FULL) {
+    if constexpr (FULL && staged_tile<MODE, DT, E, R>()) {
+      load_tile_staged<E, NTX>(static_cast<const float*>(a.x), t0, v[r]);
+    } else if constexpr (FULL) {
       constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
-      load_vec<DT, E, NTX && stream_capable<MODE, DT, E>()>(a.x, t0, off, v[r]);
+      load_vec<DT, E, NTX && E == 4 && stream_capable<MODE, DT, E, R>()>(a.x, t0, off, v[r]);
       if constexpr (RMW) load_vec<kF32, E>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, E>(a.x2, t0, off, w);
     } else {

@@ -52,7 +52,7 @@ __device__ __forceinline__ void row_load(const QuantArgs& a, int64_t t0, float (
     float w[4];
     if constexpr (FULL) {
       constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
-      load_vec<DT, 4, NTX && stream_capable<MODE, DT, 4>()>(a.x, t0, off, v[r]);
+      load_vec<DT, 4, NTX && stream_capable<MODE, DT, 4, 1>()>(a.x, t0, off, v[r]);
       if constexpr (RMW) load_vec<kF32, 4>(a.resid, t0, off, w);
       if constexpr (MODE == kWeightDiff) load_vec<DT, 4>(a.x2, t0, off, w);
     } else {
