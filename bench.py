@@ -84,9 +84,13 @@ METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HB
 
 # demangled kernel names as rocprofv3 reports them
 def kname_quant(bits, log2b, sr, dt, mode, tail=False, stream=False):
-    """stream: the non-temporal-input form (plain binary32 compress at 1 and 8
-    bits without LOWBIT_HINT_INPUT_REUSED)."""
-    ntx = str(bool(stream) and mode == 0 and dt == 0 and bits in (1, 8) and not tail).lower()
+    """stream: the non-temporal-input form, taken by a plain binary32 compress
+    without LOWBIT_HINT_INPUT_REUSED where a lane's elements of a block lie in
+    one row of code words (4 codes per word, or blocks of at most 64 words)."""
+    e = 32 // bits
+    rows = max(1, (1 << log2b) // (64 * e)) if bits > 1 else 1
+    ntx = str(bool(stream) and mode == 0 and dt == 0 and (e == 4 or rows == 1)
+              and not tail).lower()
     if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
         return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}, {ntx}>" \
                f"(lowbit::QuantArgs, long)"
@@ -97,12 +101,16 @@ def kname_quant(bits, log2b, sr, dt, mode, tail=False, stream=False):
            f"{str(tail).lower()}, {ntx}>(lowbit::QuantArgs, long)"
 
 
-def kname_reduce(in_bits, bits, log2b, sr, ef=False, tail=False):
-    if in_bits == bits == 4 and ef:     # 4-bit reduce with a residual: the row layout
+def kname_reduce(in_bits, bits, log2b, sr, ef=False, tail=False, sum_out=False, stream=True):
+    """stream: the form that reads the peers' code words non-temporally (main
+    kernel without LOWBIT_HINT_INPUT_REUSED)."""
+    st = str(bool(stream) and not tail).lower()
+    # 4-bit reduce with a residual or a binary32 sum output: the row layout
+    if in_bits == bits == 4 and (ef or sum_out):
         return f"void lowbit::rowr_kernel<{bits}, {log2b}, {str(sr).lower()}, " \
-               f"{str(ef).lower()}, {str(tail).lower()}>(lowbit::ReduceArgs, long)"
+               f"{str(ef).lower()}, {str(tail).lower()}, {st}>(lowbit::ReduceArgs, long)"
     return f"void lowbit::reduce_kernel<{in_bits}, {bits}, {log2b}, {str(sr).lower()}, " \
-           f"{str(ef).lower()}, {str(tail).lower()}>(lowbit::ReduceArgs, long)"
+           f"{str(ef).lower()}, {str(tail).lower()}, {st}>(lowbit::ReduceArgs, long)"
 
 
 def kname_hadamard_dequant(bits, log2b):
@@ -111,6 +119,15 @@ def kname_hadamard_dequant(bits, log2b):
 
 def kname_dequant(bits, apply, dt):
     return f"void lowbit::dequant_kernel<{bits}, {apply}, {dt}>(lowbit::DequantArgs)"
+
+
+KNAME_XOR = "lowbit::xor_streams_kernel(lowbit::XorArgs)"
+KNAME_COPY = "lowbit::copy_kernel(float const*, float*, long)"
+KNAME_ADD = "lowbit::add_inplace_kernel(float const*, float*, long)"
+
+
+def kname_fold(bits):
+    return f"void lowbit::fold_kernel<{bits}>(float const*, long, unsigned int*, long)"
 
 
 def source_digest() -> str:
@@ -154,6 +171,11 @@ def main() -> int:
     ap.add_argument("--cpu-configs", type=int, default=1,
                     help="with --cpu-sample > 0, also time the CPU oracle on each workload "
                          "configuration, one thread and all threads (1) or not (0)")
+    ap.add_argument("--only", default=None,
+                    help="run only these measurements, '|'-separated: a group (next_rows, "
+                         "configs, compress_pattern) or one entry of next_rows or configs by its "
+                         "name; prints them as one JSON line instead of the step (for profiling "
+                         "one workload at a time)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -183,6 +205,8 @@ def main() -> int:
     resid = torch.zeros(N, dtype=torch.float32, device=dev)
     y = torch.empty(N, dtype=torch.float32, device=dev)
     w_out = torch.empty_like(w_prev)
+    if args.only:
+        return run_only(args.only, L, lib, dev, stream, x, y)
 
     def qp(bits, block, sr=False, seed=0, off=0, hints=0):
         return L.QParams(bits, block, int(sr), hints, seed, off)
@@ -223,11 +247,12 @@ def main() -> int:
         spp = (P * PEERS)(*[scales.data_ptr() + p * snb * 2 for p in range(PEERS)])
         rc = torch.empty(snw, dtype=torch.int32, device=dev)
         rs = torch.empty(snb, dtype=torch.float16, device=dev)
-        qi, qo = qp(b, BLOCK), qp(b, BLOCK)
+        # the decompress reads the same codes right after the reduce
+        qi, qo = qp(b, BLOCK, hints=L.HINT_INPUT_REUSED), qp(b, BLOCK)
         keep += [cp, spp, rc, rs, qi, qo]
         a = (ctypes.cast(cp, P), ctypes.cast(spp, P), PEERS, share, ctypes.byref(qi),
              ctypes.byref(qo), P(rc.data_ptr()), P(rs.data_ptr()), None)
-        stages.append((f"reduce_requant b{b}", kname_reduce(b, b, 8, False),
+        stages.append((f"reduce_requant b{b}", kname_reduce(b, b, 8, False, stream=False),
                        (PEERS + 1) * (snw * 4 + snb * 2), (lib.lowbit_reduce_requant, a)))
 
         qd = qp(b, BLOCK)
@@ -491,10 +516,39 @@ def main() -> int:
     return 0
 
 
-def measure_next_rows(L, lib, dev, stream, x, reps=20):
+def run_only(spec, L, lib, dev, stream, x, y):
+    """The measurements named in `spec` and nothing else, printed as one JSON
+    line: {"only": names, "copy_us", <group>: {entry: ...}}.  A plain copy of
+    the 64 Mi binary32 bucket runs first, once, so that a byte-counter run of
+    this command holds its own calibration kernel."""
+    import torch
+    names = [t.strip() for t in spec.split("|") if t.strip()]
+    P = ctypes.c_void_p
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    st = lib.lowbit_copy_f32(P(x.data_ptr()), P(y.data_ptr()), x.numel(), sh)
+    e1.record(stream)
+    if st != 0:
+        raise L.LowbitError(st, "lowbit_copy_f32")
+    torch.cuda.synchronize()
+    out = {"only": names, "copy_us": round(e0.elapsed_time(e1) * 1e3, 2)}
+
+    def want(group):
+        return lambda name: group in names or name in names
+    out["next_rows"] = measure_next_rows(L, lib, dev, stream, x, want=want("next_rows"))
+    out["configs"] = measure_configs(L, dev, want=want("configs"))
+    if "compress_pattern" in names:
+        out["compress_pattern"] = measure_compress_pattern(L, dev, x)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure_next_rows(L, lib, dev, stream, x, reps=20, want=None):
     """Kernels of the extensions beyond the step (not part of `value`): each
     timed alone with HIP events on `stream`, median of `reps` launches, every
     launch after a 1 GiB read that leaves the Infinity Cache clean.
+    `want(name)` false: that entry is skipped.
     Returns {name: {"workload", "us", "alg_bytes", "alg_GBps", "frac"}}."""
     import torch
     from weight_communication_compression_amd import synth
@@ -509,6 +563,8 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20):
         return L.QParams(bits, block, int(sr), 0, seed, off)
 
     def timed(name, workload, alg_bytes, fn, args, kernel):
+        if want is not None and not want(name):
+            return
         for _ in range(3):
             st = fn(*args)
             if st != 0:
@@ -643,18 +699,21 @@ def measure_compress_pattern(L, dev, x, reps=20):
     return out
 
 
-def measure_configs(L, dev, reps=20):
+def measure_configs(L, dev, reps=20, want=None):
     """The kernels of the other workload configurations at their full sizes,
     each timed alone (median of `reps`, every launch after a 1 GiB read that
     leaves the Infinity Cache clean).  Inputs are drawn on the GPU from seeded
-    generators with the configurations' distributions.  Not part of `value`."""
+    generators with the configurations' distributions.  Not part of `value`.
+    `want(name)` false: that entry is skipped."""
     import torch
 
     gen = torch.Generator(device=dev).manual_seed(5)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     out = {}
 
-    def timed(name, workload, alg_bytes, fn, input_bytes):
+    def timed(name, workload, alg_bytes, fn, input_bytes, kernel):
+        if want is not None and not want(name):
+            return
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -670,7 +729,8 @@ def measure_configs(L, dev, reps=20):
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
                      "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3),
-                     "input_GBps": round(input_bytes / (ms * 1e-3) / 1e9, 1)}
+                     "input_GBps": round(input_bytes / (ms * 1e-3) / 1e9, 1),
+                     "kernel": kernel, "traffic": read_traffic(kernel)}
 
     # error feedback on 128 Mi bfloat16 gradients, b4 B128 SR
     n = 128 << 20
@@ -680,7 +740,8 @@ def measure_configs(L, dev, reps=20):
     s = torch.empty(L.num_blocks(n, 128), dtype=torch.float16, device=dev)
     timed("ef_compress 128Mi bf16", f"{n} bf16 N(0,1e-4), fp32 residual, b4 B128 SR",
           n * (2 + 4 + 4) + c.numel() * 4 + s.numel() * 2,
-          lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s), n * 2)
+          lambda: L.ef_compress(g, e, 4, 128, True, 2, 0, c, s), n * 2,
+          kname_quant(4, 7, True, 1, 1))
     del g, e, c, s
 
     # local reduce of 8 peer chunks of 32 Mi, b4 B128 in and out, with the
@@ -709,35 +770,42 @@ def measure_configs(L, dev, reps=20):
         where = "separate buffers" if not lay else "one receive buffer, messages of codes + scales"
         timed(f"reduce_requant 8x32Mi{lay}", f"8 x {n} peers ({where}), b4 B128 -> b4 B128 "
               "nearest", 9 * (nw4 * 4 + nb4 * 2),
-              lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_), 8 * n * 4)
+              lambda: L.reduce_requant(pc, ps, n, 4, 128, out_codes=oc, out_scales=os_), 8 * n * 4,
+              kname_reduce(4, 4, 7, False))
         timed(f"reduce_requant 8x32Mi +sum{lay}", f"8 x {n} peers ({where}), b4 B128 -> b4 B128 "
               "nearest, fp32 sum written", 9 * (nw4 * 4 + nb4 * 2) + n * 4,
               lambda: L.reduce_requant(pc, ps, n, 4, 128, want_sum=True, out_codes=oc,
-                                       out_scales=os_, out_sum=tot), 8 * n * 4)
+                                       out_scales=os_, out_sum=tot), 8 * n * 4,
+              kname_reduce(4, 4, 7, False, sum_out=True))
         # bandwidth reference for that access pattern: XOR of the 8 peers' code
         # streams read the way the reduce reads them, one output stream, no
         # arithmetic
         timed(f"xor_streams 8x16MiB reference{lay}", f"XOR of the 8 peers' code streams "
               f"({nw4} words each, {where}) with the reduce's access pattern; not a codec step",
-              9 * nw4 * 4, lambda: L.xor_streams(pc, oc), 8 * n * 4)
-        ref = out[f"xor_streams 8x16MiB reference{lay}"]["alg_GBps"]
+              9 * nw4 * 4, lambda: L.xor_streams(pc, oc), 8 * n * 4, KNAME_XOR)
+        ref = out.get(f"xor_streams 8x16MiB reference{lay}")
         for k in (f"reduce_requant 8x32Mi{lay}", f"reduce_requant 8x32Mi +sum{lay}"):
-            out[k]["of_pattern_reference"] = round(out[k]["alg_GBps"] / ref, 3)
+            if ref is not None and k in out:
+                out[k]["of_pattern_reference"] = round(out[k]["alg_GBps"] / ref["alg_GBps"], 3)
     # the same bytes as one stream: a 128 MiB read and a 16 MiB write (the
     # compress-volume reference at 4 bits over 32 Mi binary32 values), against
     # which the eight equally long streams read at once are compared
     one = recv[:8 * nw4].view(torch.float32)
     timed("fold 128MiB one-stream reference", "one contiguous 128 MiB read, 16 MiB written "
           "(compress-volume reference kernel); not a codec step", 9 * nw4 * 4,
-          lambda: L.fold_f32(one, 4, oc), 8 * n * 4)
-    one_gbps = out["fold 128MiB one-stream reference"]["alg_GBps"]
+          lambda: L.fold_f32(one, 4, oc), 8 * n * 4, kname_fold(4))
+    one_ref = out.get("fold 128MiB one-stream reference")
     for lay in layouts:
         k = f"xor_streams 8x16MiB reference{lay}"
-        out[k]["of_one_stream"] = round(out[k]["alg_GBps"] / one_gbps, 3)
+        if one_ref is not None and k in out:
+            out[k]["of_one_stream"] = round(out[k]["alg_GBps"] / one_ref["alg_GBps"], 3)
     del layouts, recv, oc, os_, tot, one
 
     # weight difference on an 840 Mi bfloat16 shard, b4 B64
     n = 840 << 20
+    if want is not None and not (want("wdiff_compress 840Mi bf16") or
+                                 want("wdiff_apply 840Mi bf16")):
+        return out
     w_prev = (torch.randn(n, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
     w_new = (w_prev.float() + torch.randn(n, device=dev, generator=gen) * 1e-4).to(torch.bfloat16)
     c = torch.empty(L.num_words(n, 4), dtype=torch.int32, device=dev)
@@ -745,9 +813,11 @@ def measure_configs(L, dev, reps=20):
     w_out = torch.empty_like(w_prev)
     wb = n * 4 + c.numel() * 4 + s.numel() * 2
     timed("wdiff_compress 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
-          lambda: L.wdiff_compress(w_new, w_prev, 4, 64, codes=c, scales=s), n * 4)
+          lambda: L.wdiff_compress(w_new, w_prev, 4, 64, codes=c, scales=s), n * 4,
+          kname_quant(4, 6, False, 1, 2))
     timed("wdiff_apply 840Mi bf16", f"{n} bf16 weights, b4 B64", wb,
-          lambda: L.wdiff_apply(w_prev, c, s, 4, 64, out=w_out), n * 2)
+          lambda: L.wdiff_apply(w_prev, c, s, 4, 64, out=w_out), n * 2,
+          kname_dequant(4, 1, 1))
     del w_prev, w_new, c, s, w_out
     torch.cuda.synchronize()
     return out

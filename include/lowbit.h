@@ -91,12 +91,15 @@ typedef enum {
 /* Quantizer options (bitscom README, "Backend Registration Options": bitwidth
  * and block size; "Implemented Features": stochastic rounding). */
 
-/* lowbit_qparams.hints: the caller reads the compress input again soon (for
- * example it compresses the same buffer at another bitwidth next): keep it in
- * the caches.  Without it a compress streams its input where its access
- * pattern allows (non-temporal loads: binary32 input at 1 and 8 bits in the
- * plain compress), which is faster for a buffer compressed once.  Accepted by
- * every entry point; the others ignore it. */
+/* lowbit_qparams.hints: the caller reads the input again soon (for example
+ * it compresses the same buffer at another bitwidth next, or decompresses the
+ * peers' codes after reducing them): keep it in the caches.  Without it the
+ * input is streamed where the access pattern allows (non-temporal loads), which
+ * is faster for data read once: the binary32 input of the plain compress
+ * (lowbit_quantize_pack: at 1 and 8 bits, and at 2 and 4 bits when a block
+ * spans at most 64 code words) and the peers' code words of the local reduce
+ * (taken from in_p of lowbit_reduce_requant and lowbit_reduce_requant_ef).
+ * Accepted by every entry point; the others ignore it. */
 #define LOWBIT_HINT_INPUT_REUSED 1
 typedef struct {
     int32_t  bitwidth;        /* b: 1, 2, 4 or 8                                */

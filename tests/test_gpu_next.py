@@ -103,7 +103,7 @@ def test_reduce_stage2_ef_chained(bits, B, sr, P, want_sum):
     for rnd in range(2):
         say(f"reduce_ef bits={bits} B={B} sr={sr} P={P} sum={want_sum} n={n} round={rnd}")
         c, s, tot = L.reduce_requant_ef(gc, gs, n, bits, B, e_gpu, sr, 9 + rnd, B * 4,
-                                        want_sum=want_sum)
+                                        want_sum=want_sum, input_reused=rnd == 1)
         torch.cuda.synchronize()
         wc, ws, wt, e_cpu = O.reduce_requant_ex(pcs, pss, n, bits, B, bits, B, sr, 9 + rnd,
                                                 B * 4, residual=e_cpu, want_sum=True)
@@ -128,7 +128,7 @@ def test_reduce_mixed(widths, blocks, sr, ef):
     Bi, Bo = blocks
     P = 5
     T = max(_tile(bo, Bo), Bi)
-    for n in (3 * T + 37, 2 * T, 64 * (32 // bo) + 3):
+    for k, n in enumerate((3 * T + 37, 2 * T, 64 * (32 // bo) + 3)):
         pcs, pss, gc, gs = _peers(P, n, bi, Bi, 700 + bi + bo)
         e_cpu = (np.random.default_rng(n).standard_normal(n) * 1e-2).astype(np.float32) \
             if ef else None
@@ -136,10 +136,11 @@ def test_reduce_mixed(widths, blocks, sr, ef):
         if ef:
             e_gpu = f32_to_gpu(e_cpu)
             c, s, tot = L.reduce_requant_ef(gc, gs, n, bi, Bi, e_gpu, sr, 4, 0, want_sum=True,
-                                            out_bitwidth=bo, out_block_size=Bo)
+                                            out_bitwidth=bo, out_block_size=Bo,
+                                            input_reused=k == 1)
         else:
             c, s, tot = L.reduce_requant(gc, gs, n, bi, Bi, sr, 4, 0, want_sum=True,
-                                         out_bitwidth=bo, out_block_size=Bo)
+                                         out_bitwidth=bo, out_block_size=Bo, input_reused=k == 1)
         torch.cuda.synchronize()
         wc, ws, wt, we = O.reduce_requant_ex(pcs, pss, n, bi, Bi, bo, Bo, sr, 4, 0,
                                              residual=e_cpu, want_sum=True)

@@ -51,7 +51,8 @@ def _device():
 @pytest.mark.parametrize("bits", BITS)
 def test_quantize_input_reused_hint(bits, B, sr):
     """LOWBIT_HINT_INPUT_REUSED selects cached rather than streamed loads of
-    the input (1 and 8 bits, binary32); the codes and scales are the same."""
+    the binary32 input (where the tile shape streams it); the codes and scales
+    are the same."""
     for i, n in enumerate(_sizes(bits, B)):
         x = _input("mixed", n, 7000 * bits + B + i, "f32")
         say(f"quantize (input reused) bits={bits} B={B} sr={sr} n={n}")
@@ -142,8 +143,10 @@ def test_reduce_requant(bits, B, sr, P, want_sum):
         pss.append(s)
         gc.append(torch.from_numpy(c.view(np.int32)).cuda())
         gs.append(torch.from_numpy(s.view(np.float16)).cuda())
-    say(f"reduce bits={bits} B={B} sr={sr} P={P} sum={want_sum} n={n}")
-    c, s, tot = L.reduce_requant(gc, gs, n, bits, B, sr, 9, B * 5, want_sum=want_sum)
+    reused = P % 2 == 1      # LOWBIT_HINT_INPUT_REUSED: cached rather than streamed code loads
+    say(f"reduce bits={bits} B={B} sr={sr} P={P} sum={want_sum} reused={reused} n={n}")
+    c, s, tot = L.reduce_requant(gc, gs, n, bits, B, sr, 9, B * 5, want_sum=want_sum,
+                                 input_reused=reused)
     torch.cuda.synchronize()
     wc, ws, wt = O.reduce_requant(pcs, pss, n, bits, B, bits, sr, 9, B * 5, want_sum=True)
     assert_same(scales_np(s), ws, "scales")
@@ -206,8 +209,9 @@ def test_reduce_eight_peers_exact_sums(bits, B, sr, kind):
         gs.append(torch.from_numpy(s.view(np.float16)).cuda())
     say(f"reduce 8 peers bits={bits} B={B} sr={sr} kind={kind} n={n}")
     wc, ws, wt = O.reduce_requant(pcs, pss, n, bits, B, bits, sr, 3, 0, want_sum=True)
-    for want_sum in (False, True):
-        c, s, tot = L.reduce_requant(gc, gs, n, bits, B, sr, 3, 0, want_sum=want_sum)
+    for want_sum, reused in ((False, False), (True, False), (False, True)):
+        c, s, tot = L.reduce_requant(gc, gs, n, bits, B, sr, 3, 0, want_sum=want_sum,
+                                     input_reused=reused)
         torch.cuda.synchronize()
         assert_same(scales_np(s), ws, "scales")
         assert_same(codes_np(c), wc, "codes")

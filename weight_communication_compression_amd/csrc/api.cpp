@@ -205,9 +205,11 @@ lowbit_status reduce_common(const uint32_t* const* peer_codes, const uint16_t* c
   a.resid = residual;
   a.out = TileOut{out_codes, out_scales, out_p->index_offset, seed_key(out_p->seed)};
   const bool sr = out_p->stochastic != 0;
-  if (mixed) return launch_reduce_mixed(bi, bo, lb, sr, want_residual, a, stream);
-  return want_residual ? launch_reduce_same_ef(bo, lb, sr, a, stream)
-                       : launch_reduce_same(bo, lb, sr, a, stream);
+  // the peers' code words are streamed unless the caller reads them again
+  const bool si = (in_p->hints & LOWBIT_HINT_INPUT_REUSED) == 0;
+  if (mixed) return launch_reduce_mixed(bi, bo, lb, sr, want_residual, si, a, stream);
+  return want_residual ? launch_reduce_same_ef(bo, lb, sr, si, a, stream)
+                       : launch_reduce_same(bo, lb, sr, si, a, stream);
 }
 
 }  // namespace

@@ -6,7 +6,7 @@ namespace lowbit {
 
 template <int BITS, int APPLY, int DT>
 static lowbit_status launch_d(const DequantArgs& a, hipStream_t s) {
-  constexpr int ROWS = dequant_rows<APPLY>();
+  constexpr int ROWS = dequant_rows<BITS, APPLY>();
   constexpr int ROW = kWave * dequant_epl<APPLY>();
   const int64_t nrows = (a.n + ROW - 1) / ROW;
   const int64_t ntrips = (nrows + ROWS - 1) / ROWS;

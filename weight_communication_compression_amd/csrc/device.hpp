@@ -92,6 +92,19 @@ __device__ __forceinline__ int64_t logical_block() {
   }
 }
 
+// A pointer to device memory that is the same in every lane, held in scalar
+// registers (as a global-memory pointer, so that loads through it stay
+// global loads).
+template <typename T>
+using global_ptr = const __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ global_ptr<T> uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (global_ptr<T>)(((uint64_t)hi << 32) | lo);
+}
+
 // Index of this wave in the grid, as a wave-uniform (scalar) value: element
 // offsets then split into a scalar base and a 32-bit per-lane offset, and
 // loads and stores use the scalar-base addressing mode.  THREADS: the

@@ -50,13 +50,14 @@ lowbit_status launch_quantize_ef21(int bits, int log2b, bool sr, int dt, bool st
 lowbit_status launch_quantize_hadamard(int bits, int log2b, bool sr, int dt, bool stream_input,
                                        const QuantArgs& a, hipStream_t s);
 // local reduce: same width in and out, without / with a stage-2 residual;
-// mixed widths (in_bits > bits) for the pairs 8->4, 8->2, 4->2
-lowbit_status launch_reduce_same(int bits, int log2b, bool sr, const ReduceArgs& a,
-                                 hipStream_t s);
-lowbit_status launch_reduce_same_ef(int bits, int log2b, bool sr, const ReduceArgs& a,
-                                    hipStream_t s);
+// mixed widths (in_bits > bits) for the pairs 8->4, 8->2, 4->2.
+// stream_input: read the peers' code words non-temporally.
+lowbit_status launch_reduce_same(int bits, int log2b, bool sr, bool stream_input,
+                                 const ReduceArgs& a, hipStream_t s);
+lowbit_status launch_reduce_same_ef(int bits, int log2b, bool sr, bool stream_input,
+                                    const ReduceArgs& a, hipStream_t s);
 lowbit_status launch_reduce_mixed(int in_bits, int bits, int log2b, bool sr, bool ef,
-                                  const ReduceArgs& a, hipStream_t s);
+                                  bool stream_input, const ReduceArgs& a, hipStream_t s);
 lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a, hipStream_t s);
 // decompress + inverse Hadamard, blocks of 32 .. 4096
 lowbit_status launch_hadamard_dequant(int bits, const DequantArgs& a, hipStream_t s);

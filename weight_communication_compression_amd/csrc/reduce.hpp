@@ -70,22 +70,30 @@ __device__ __forceinline__ void accumulate_word(uint32_t word, float s, float* a
 template <int IN_BITS, int BITS>
 constexpr int in_words() { return IN_BITS / BITS; }
 
-template <int M>
+// Load *p: STREAM, non-temporally (the caller reads the line once).
+template <bool STREAM, typename T>
+__device__ __forceinline__ T load_once(const T* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// M consecutive code words of one peer.
+template <int M, bool STREAM>
 __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   if constexpr (M == 1) {
-    w[0] = *p;
+    w[0] = load_once<STREAM>(p);
   } else if constexpr (M == 2) {
     const u32x2* q = reinterpret_cast<const u32x2*>(p);
-    const u32x2 t = *q;
+    const u32x2 t = load_once<STREAM>(q);
     w[0] = t.x;
     w[1] = t.y;
   } else {
 #pragma unroll
     for (int k = 0; k < M / 4; ++k) {
       const u32x4* q = reinterpret_cast<const u32x4*>(p) + k;
-      const u32x4 t = *q;
+      const u32x4 t = load_once<STREAM>(q);
       w[4 * k + 0] = t.x;
       w[4 * k + 1] = t.y;
       w[4 * k + 2] = t.z;
@@ -121,7 +129,7 @@ __device__ __forceinline__ int peer_count(const ReduceArgs& a) {
 // a trip.  The pointers of all G peers are read first (the argument block
 // holds kMaxPeers entries and g + G <= kMaxPeers), so that their scalar loads
 // are not each waited for between the vector loads of two peers.
-template <int IN_BITS, int BITS, int R, int W, int G, bool GUARD, int NPC>
+template <int IN_BITS, int BITS, int R, int W, int G, bool GUARD, int NPC, bool STREAM>
 __device__ __forceinline__ void load_peer_group(const ReduceArgs& a, int g, const int64_t* wt,
                                                 const int64_t* kt, const uint32_t* wl,
                                                 const uint32_t* kl, const bool* in,
@@ -153,7 +161,7 @@ __device__ __forceinline__ void load_peer_group(const ReduceArgs& a, int g, cons
           for (int m = 0; m < M; ++m) w[q][i][m] = (in[i] && w0 + m < nwin) ? cp[w0 + m] : 0u;
           sc[q][i] = in[i] ? (sp + kt[i / R])[kl[i]] : 0u;
         } else {
-          load_words<M>(cp + wt[i / R] + wl[i] * M, w[q][i]);
+          load_words<M, STREAM>(cp + wt[i / R] + wl[i] * M, w[q][i]);
           sc[q][i] = (sp + kt[i / R])[kl[i]];
         }
       }
@@ -356,7 +364,7 @@ __device__ __forceinline__ float pow2_f32(int x) { return __uint_as_float((uint3
 // Loads and peer sums of one trip of NT full tiles for exactly eight peers
 // (exact_path): acc as decode_peer_group leaves it, i.e. 2^acc_shift<BITS>()
 // times the peer-ordered binary32 sums.
-template <int BITS, int LOG2B, int NT>
+template <int BITS, int LOG2B, int NT, bool STREAM>
 __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t* wt,
                                              const int64_t* kt, const uint32_t* wl,
                                              const uint32_t* kl, float (*acc)[Grid<BITS>::E]) {
@@ -374,16 +382,24 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
 #pragma unroll
   for (int q = 0; q < 8; ++q)
 #pragma unroll
-    for (int i = 0; i < W; ++i) w[q][i][0] = (cps[q] + wt[i / R])[wl[i]];
+    for (int i = 0; i < W; ++i) w[q][i][0] = load_once<STREAM>(cps[q] + wt[i / R] + wl[i]);
   // one scale per lane and slot: peer p's scale of the lane's block (a block
-  // spans at least 8 lanes, so each aligned group of 8 lanes holds all eight)
-  const uint16_t* s01 = (p & 1) ? a.scales[1] : a.scales[0];
-  const uint16_t* s23 = (p & 1) ? a.scales[3] : a.scales[2];
-  const uint16_t* s45 = (p & 1) ? a.scales[5] : a.scales[4];
-  const uint16_t* s67 = (p & 1) ? a.scales[7] : a.scales[6];
-  const uint16_t* s03 = (p & 2) ? s23 : s01;
-  const uint16_t* s47 = (p & 2) ? s67 : s45;
-  const uint16_t* sp = (p & 4) ? s47 : s03;
+  // spans at least 8 lanes, so each aligned group of 8 lanes holds all eight).
+  // The eight pointers are made wave-uniform first, so that they are read
+  // with the scalar loads of the argument block and selected per lane in
+  // registers; a per-lane choice among argument-block slots would otherwise
+  // become a vector load of the pointer, which the code word loads then wait
+  // behind.
+  global_ptr<uint16_t> sq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) sq[q] = uniform_ptr(a.scales[q]);
+  const global_ptr<uint16_t> s01 = (p & 1) ? sq[1] : sq[0];
+  const global_ptr<uint16_t> s23 = (p & 1) ? sq[3] : sq[2];
+  const global_ptr<uint16_t> s45 = (p & 1) ? sq[5] : sq[4];
+  const global_ptr<uint16_t> s67 = (p & 1) ? sq[7] : sq[6];
+  const global_ptr<uint16_t> s03 = (p & 2) ? s23 : s01;
+  const global_ptr<uint16_t> s47 = (p & 2) ? s67 : s45;
+  const global_ptr<uint16_t> sp = (p & 4) ? s47 : s03;
   uint32_t s16[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) s16[i] = (sp + kt[i / R])[kl[i]];
@@ -468,7 +484,8 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
 // may reach past the end of the buffer (only in the tail kernel): loads past
 // the end read 0 and those positions are +0 for the statistic.  EF: stage-2
 // error feedback with the residual a.resid.
-template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD, int NPC = 0>
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, int NT, bool GUARD, int NPC = 0,
+          bool STREAM = false>
 __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R, W = NT * R;
@@ -483,19 +500,20 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
   if constexpr (EF) load_residual<BITS, LOG2B, NT, GUARD>(a, tile0, e);
   float acc[NT][R][E];
   if constexpr (!GUARD && exact_path<IN_BITS, BITS, LOG2B, NPC>()) {
-    reduce8_sums<BITS, LOG2B, NT>(a, wt, kt, wl, kl, &acc[0][0]);
+    reduce8_sums<BITS, LOG2B, NT, STREAM>(a, wt, kt, wl, kl, &acc[0][0]);
   } else if constexpr (NPC > 0) {
 #pragma unroll
     for (int g = 0; g < NPC; g += G) {
       uint32_t w[G][W][M], sc[G][W];
-      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, NPC>(a, g, wt, kt, wl, kl, in, w, sc);
+      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, NPC, STREAM>(a, g, wt, kt, wl, kl, in, w,
+                                                                  sc);
       decode_peer_group<IN_BITS, BITS, W, G, NPC>(a, g, w, sc, &acc[0][0]);
     }
   } else {
 #pragma unroll 1
     for (int g = 0; g < a.npeers; g += G) {
       uint32_t w[G][W][M], sc[G][W];
-      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, 0>(a, g, wt, kt, wl, kl, in, w, sc);
+      load_peer_group<IN_BITS, BITS, R, W, G, GUARD, 0, STREAM>(a, g, wt, kt, wl, kl, in, w, sc);
       decode_peer_group<IN_BITS, BITS, W, G, 0>(a, g, w, sc, &acc[0][0]);
     }
   }
@@ -508,7 +526,8 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
 // (Measured: a grid of a few workgroups per CU whose waves walk several trips
 // and issue the next trip's loads before decoding the current one is 30 %
 // slower on 8 x 32 Mi peers than one trip per wave.)
-template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL>
+// STREAM: the peers' code words are read non-temporally (main kernel only).
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL, bool STREAM = false>
 __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
@@ -526,12 +545,14 @@ __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int
     // was capped (more than 2^32 work-items), so the first trip is kept out
     // of it and its addresses are not carried from trip to trip.
     if (a.npeers == 8) {
-      if (trip < ntrips) reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 8>(a, trip * U);
+      if (trip < ntrips)
+        reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 8, STREAM>(a, trip * U);
     } else {
-      if (trip < ntrips) reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0>(a, trip * U);
+      if (trip < ntrips)
+        reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0, STREAM>(a, trip * U);
     }
     for (int64_t t = trip + nwaves; t < ntrips; t += nwaves)
-      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0>(a, t * U);
+      reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 0, STREAM>(a, t * U);
   }
 }
 

@@ -34,13 +34,17 @@ namespace lowbit {
 // error-feedback / EF21 modes
 constexpr int kRowRows = 2;
 constexpr int kRowRowsEf = 1;
+template <int MODE>
+constexpr int row_rows_min() {
+  return (MODE == kErrorFeedback || MODE == kEF21) ? kRowRowsEf : kRowRows;
+}
 
-template <int BITS, int LOG2B, int MODE>
+// RMIN: rows per trip when blocks are shorter than that (a caller with other
+// loads in flight per row may choose its own)
+template <int BITS, int LOG2B, int MODE, int RMIN = row_rows_min<MODE>()>
 struct RowShape {
   static constexpr int B = 1 << LOG2B;
   static constexpr int ROW = kWave * 4;                  // elements per row
-  static constexpr int RMIN =
-      (MODE == kErrorFeedback || MODE == kEF21) ? kRowRowsEf : kRowRows;
   static constexpr int RT = B > RMIN * ROW ? B / ROW : RMIN;   // rows per trip
   static constexpr int TILE = ROW * RT;
   static constexpr int LB = B >= ROW ? kWave : B / 4;    // lanes of a block within a row
@@ -50,12 +54,12 @@ struct RowShape {
 
 // Codes, scales and (error feedback / EF21) the residual or state of one
 // loaded trip of RT rows.
-template <int BITS, int LOG2B, bool SR, int MODE, bool FULL>
-__device__ __forceinline__ void row_finish(const QuantArgs& a, int64_t t0,
-                                           const float (&v)[RowShape<BITS, LOG2B, MODE>::RT][4],
-                                           const float (&h)[RowShape<BITS, LOG2B, MODE>::RT][4]) {
+template <int BITS, int LOG2B, bool SR, int MODE, bool FULL, int RMIN = row_rows_min<MODE>()>
+__device__ __forceinline__ void row_finish(
+    const QuantArgs& a, int64_t t0, const float (&v)[RowShape<BITS, LOG2B, MODE, RMIN>::RT][4],
+    const float (&h)[RowShape<BITS, LOG2B, MODE, RMIN>::RT][4]) {
   using G = Grid<BITS>;
-  using S = RowShape<BITS, LOG2B, MODE>;
+  using S = RowShape<BITS, LOG2B, MODE, RMIN>;
   constexpr int RT = S::RT, RB = S::RB, LB = S::LB, B = S::B, LPW = S::LPW;
   constexpr float QMAX = (float)G::QMAX;
   constexpr bool WANT_DEQ = MODE == kErrorFeedback || MODE == kEF21;

@@ -43,10 +43,20 @@ __device__ __forceinline__ void accumulate_piece(uint32_t piece, float s, float*
 // measured as fast or faster for them.
 constexpr int kRowrXcdChunk = 8;
 
-template <int BITS, int LOG2B, bool SR, bool EF, bool FULL, int NPC = 0>
+// Rows of 256 per trip for blocks shorter than that: 2 in both modes.  With
+// the stage-2 residual (8 x 32 Mi peers, b4 B128) 2 rows take 66.8 us against
+// 70.5 us for the single row of the error-feedback compress, whose trip has
+// no peer loads to keep in flight, and 68.8 us for 4 rows.  Streamed peers'
+// code words (non-temporal loads, without LOWBIT_HINT_INPUT_REUSED): the
+// reduce with the binary32 sum output 60 -> 56 us, the stage-2 one unchanged.
+constexpr int kRowrRows = 2;
+template <int BITS, int LOG2B, bool EF>
+using RowrShape = RowShape<BITS, LOG2B, EF ? kErrorFeedback : kPlain, kRowrRows>;
+
+template <int BITS, int LOG2B, bool SR, bool EF, bool FULL, int NPC = 0, bool STREAM = false>
 __device__ __forceinline__ void rowr_trip(const ReduceArgs& a, int64_t t0) {
   constexpr int MODE = EF ? kErrorFeedback : kPlain;
-  using S = RowShape<BITS, LOG2B, MODE>;
+  using S = RowrShape<BITS, LOG2B, EF>;
   // peers whose loads are in flight together: 8, fewer for trips of more
   // than two rows, so that a lane holds at most 16 code words and 16 scales
   constexpr int RT = S::RT, E = Grid<BITS>::E, G = RT <= 2 ? 8 : (16 / RT > 1 ? 16 / RT : 1);
@@ -92,7 +102,7 @@ __device__ __forceinline__ void rowr_trip(const ReduceArgs& a, int64_t t0) {
           w[q][r] = 0;
           sc[q][r] = 0;
           if (FULL || i0 < n) {
-            w[q][r] = cp[i0 / E];
+            w[q][r] = load_once<STREAM>(cp + i0 / E);
             sc[q][r] = sp[i0 >> lbi];
           }
         }
@@ -139,16 +149,17 @@ __device__ __forceinline__ void rowr_trip(const ReduceArgs& a, int64_t t0) {
   qa.n = n;
   qa.resid = a.resid;
   qa.out = a.out;
-  row_finish<BITS, LOG2B, SR, MODE, FULL>(qa, t0, v, h);
+  row_finish<BITS, LOG2B, SR, MODE, FULL, kRowrRows>(qa, t0, v, h);
   (void)h;
 }
 
 // Main kernel (TAIL = false): one full trip per wave; the grid covers the
 // `first` full trips.  Tail kernel (TAIL = true, one wave): the trips from
 // `first` on, the last of which may be partial.
-template <int BITS, int LOG2B, bool SR, bool EF, bool TAIL>
+// STREAM: the peers' code words are read non-temporally (main kernel only).
+template <int BITS, int LOG2B, bool SR, bool EF, bool TAIL, bool STREAM = false>
 __global__ __launch_bounds__(kBlockThreads) void rowr_kernel(ReduceArgs a, int64_t first) {
-  using S = RowShape<BITS, LOG2B, EF ? kErrorFeedback : kPlain>;
+  using S = RowrShape<BITS, LOG2B, EF>;
   if constexpr (TAIL) {
     if (global_wave_id() != 0) return;
     const int64_t ntrips = (a.n + S::TILE - 1) / S::TILE;
@@ -164,11 +175,11 @@ __global__ __launch_bounds__(kBlockThreads) void rowr_kernel(ReduceArgs a, int64
     // The first trip is kept out of the loop (see for_each_trip), which only
     // runs where the grid was capped.
     if (trip < first) {
-      if (a.npeers == 8) rowr_trip<BITS, LOG2B, SR, EF, true, 8>(a, trip * S::TILE);
-      else rowr_trip<BITS, LOG2B, SR, EF, true, 0>(a, trip * S::TILE);
+      if (a.npeers == 8) rowr_trip<BITS, LOG2B, SR, EF, true, 8, STREAM>(a, trip * S::TILE);
+      else rowr_trip<BITS, LOG2B, SR, EF, true, 0, STREAM>(a, trip * S::TILE);
     }
     for (int64_t t = trip + nwaves; t < first; t += nwaves)
-      rowr_trip<BITS, LOG2B, SR, EF, true, 0>(a, t * S::TILE);
+      rowr_trip<BITS, LOG2B, SR, EF, true, 0, STREAM>(a, t * S::TILE);
   }
 }
 

@@ -257,7 +257,8 @@ def ef21_compress(g: torch.Tensor, state: torch.Tensor, bitwidth: int, block_siz
 
 
 def _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed, index_offset,
-            out_codes, out_scales, out_sum, want_sum, out_bitwidth, out_block_size, residual):
+            out_codes, out_scales, out_sum, want_sum, out_bitwidth, out_block_size, residual,
+            input_reused=False):
     P = len(peer_codes)
     if P != len(peer_scales):
         raise LowbitError(EINVAL, "peer_codes and peer_scales differ in length")
@@ -277,7 +278,7 @@ def _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed, 
         raise LowbitError(EINVAL, "out_sum must be float32 with >= n elements")
     cp = (ctypes.c_void_p * P)(*[_dev(c, "peer codes") for c in peer_codes])
     sp = (ctypes.c_void_p * P)(*[_dev(s, "peer scales") for s in peer_scales])
-    qi = _qp(bitwidth, block_size)
+    qi = _qp(bitwidth, block_size, hints=HINT_INPUT_REUSED if input_reused else 0)
     qo = _qp(ob, oB, stochastic, seed, index_offset)
     tail = (_dev(out_codes, "out_codes"), _dev(out_scales, "out_scales"),
             _dev(out_sum, "out_sum") if out_sum is not None else None, _stream(like))
@@ -301,30 +302,34 @@ def reduce_requant(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[tor
                    n: int, bitwidth: int, block_size: int, stochastic: bool = False,
                    seed: int = 0, index_offset: int = 0, out_codes=None, out_scales=None,
                    out_sum=None, want_sum: bool = False, out_bitwidth: Optional[int] = None,
-                   out_block_size: Optional[int] = None):
+                   out_block_size: Optional[int] = None, input_reused: bool = False):
     """Local reduce: dequantize npeers chunks packed with (bitwidth,
     block_size), sum in peer order, requantize with (out_bitwidth,
     out_block_size) (default: the same) and the rounding options.
+    input_reused: the caller reads the peers' codes again soon
+    (LOWBIT_HINT_INPUT_REUSED), so they are not streamed; results are the same.
 
     Returns (codes, scales, sum_or_None)."""
     return _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed,
                    index_offset, out_codes, out_scales, out_sum, want_sum, out_bitwidth,
-                   out_block_size, None)
+                   out_block_size, None, input_reused)
 
 
 def reduce_requant_ef(peer_codes: Sequence[torch.Tensor], peer_scales: Sequence[torch.Tensor],
                       n: int, bitwidth: int, block_size: int, residual: torch.Tensor,
                       stochastic: bool = False, seed: int = 0, index_offset: int = 0,
                       out_codes=None, out_scales=None, out_sum=None, want_sum: bool = False,
-                      out_bitwidth: Optional[int] = None, out_block_size: Optional[int] = None):
+                      out_bitwidth: Optional[int] = None, out_block_size: Optional[int] = None,
+                      input_reused: bool = False):
     """Local reduce with stage-2 error feedback: the sum plus `residual`
     (float32[n], updated in place) is requantized.  Returns (codes, scales,
-    sum_or_None); the sum is taken before the residual is added."""
+    sum_or_None); the sum is taken before the residual is added.
+    input_reused: as for reduce_requant."""
     if residual is None:
         raise LowbitError(EINVAL, "reduce_requant_ef needs a residual")
     return _reduce(peer_codes, peer_scales, n, bitwidth, block_size, stochastic, seed,
                    index_offset, out_codes, out_scales, out_sum, want_sum, out_bitwidth,
-                   out_block_size, residual)
+                   out_block_size, residual, input_reused)
 
 
 def wdiff_compress(w_new: torch.Tensor, w_old: torch.Tensor, bitwidth: int, block_size: int,
