@@ -19,10 +19,12 @@
 namespace lowbit {
 
 // output elements per lane per trip.  Measured on 8 x 32 Mi peers, b4 B128,
-// with the integer sums: 8 elements (44 VGPRs, 8 waves per SIMD) 36.0 us
-// with separately allocated peers and 35.2 us in one receive buffer; 16
-// elements (84 VGPRs) 39.2 and 34.3 us.  8 is the steadier of the two.
-constexpr int kReduceElemsPerTrip = 8;
+// with the integer sums and scalar scale pointers: 8 elements per lane 34.4
+// us with separately allocated peers and 33.1 us in one receive buffer, 16
+// elements 33.3 and 32.4 us (the per-wave set-up is shared by twice the
+// elements; the kernel issues vector-ALU work most of its time); 8-bit
+// B512 -> 4-bit B128: 52-55 us against 50.3 us.
+constexpr int kReduceElemsPerTrip = 16;
 
 template <int PER_LANE>
 constexpr int reduce_tiles_per_trip() {
@@ -428,12 +430,18 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
                            __builtin_bit_cast(u16x2, group8_lane<2>(pair)),
                            __builtin_bit_cast(u16x2, group8_lane<4>(pair)),
                            __builtin_bit_cast(u16x2, group8_lane<6>(pair))};
+      // 8 bits: sum[k] = sum_p M_p (c_pk - HALF), codes c as unsigned bytes.
+      // 4 bits: byte k of a word holds elements 2k (low nibble l) and 2k + 1
+      // (high nibble h); sum[2k + 1] = sum_p M_p 16 (h - 8) from the high
+      // nibbles in place, and sum[2k] first takes the whole bytes,
+      // sum_p M_p (l + 16 h) - 136 sum M, from which sum[2k + 1] is taken
+      // away at the end: sum_p M_p (l - 8).  (Modulo 2^32 throughout; each
+      // result is below 2^23 in magnitude, so it is exact as int32.)
       uint32_t sum[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        // 4 bits: odd elements are the high nibbles of bytes, summed 16x
-        const uint32_t f = (BITS == 4 && (j & 1)) ? 16u : 1u;
-        sum[j] = 0u - HALF * f * sumM;
+        const uint32_t f = BITS == 4 ? ((j & 1) ? 16u * HALF : 17u * HALF) : HALF;
+        sum[j] = 0u - f * sumM;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -444,14 +452,18 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
           const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
           const uint32_t b2 = __builtin_amdgcn_perm(wo, we, sel);
           if constexpr (BITS == 4) {
-            sum[2 * k] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2 & 0x000F000Fu), mp[j],
-                                                sum[2 * k], false);
+            sum[2 * k] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2), mp[j], sum[2 * k],
+                                                false);
             sum[2 * k + 1] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2 & 0x00F000F0u),
                                                     mp[j], sum[2 * k + 1], false);
           } else {
             sum[k] = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, b2), mp[j], sum[k], false);
           }
         }
+      }
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sum[2 * k] -= sum[2 * k + 1];
       }
       // binary32 sums, scaled like the binary32 path's: 2^K * S * u
       const int x = (int)(lo[i] < 30u ? lo[i] : 30u) - 25 + K;
