@@ -35,8 +35,8 @@ static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   constexpr int ROWS = hadamard_rows_per_trip<LOG2B>();
   const int64_t waves = (nrows + ROWS - 1) / ROWS;   // one trip per wave
-  return launch(&hadamard_dequant_kernel<BITS, LOG2B>, grid_for_tiles<kDeqThreads>(waves),
-                kDeqThreads, s, a);
+  return launch(&hadamard_dequant_kernel<BITS, LOG2B>, grid_for_tiles<kHsDeqThreads>(waves),
+                kHsDeqThreads, s, a);
 }
 
 template <int BITS>

@@ -177,10 +177,15 @@ __global__ __launch_bounds__((deq_threads<BITS, APPLY>())) void dequant_kernel(D
 // the lane, then lanes, then rows.  Loads and stores are guarded, the
 // transform is not (every lane of the wave takes part in the exchanges;
 // lanes past the end hold values that are not stored).  Rows per trip,
-// measured on the 64 Mi bucket at 4 bits, B = 128: 1 row 83 us, 2: 65,
-// 4: 63, 8: 60.6, 16: 75 (more rows keep more exchanges in flight per wave
-// until the register footprint costs occupancy).
-constexpr int kHsDeqRows = 8;
+// measured on the 64 Mi bucket at 4 bits, B = 128, with the exchanges on
+// ds_swizzle: 1 row 83 us, 2: 65, 4: 63, 8: 60.6, 16: 75 (more rows keep more
+// exchanges in flight per wave until the register footprint costs
+// occupancy); with DPP / permlane exchanges (flushed caches): 8 rows 56.9,
+// 4 rows 54.8 us.
+constexpr int kHsDeqRows = 4;
+constexpr bool kHsDeqDpp = true;      // cross-lane partners by DPP moves where possible
+// workgroup size: 256 threads 53.8 us against 55.2 (128) and 55.0 (64)
+constexpr int kHsDeqThreads = 256;
 template <int LOG2B>
 constexpr int hadamard_rows_per_trip() {
   return (1 << LOG2B) > kHsDeqRows * kDeqRow ? (1 << LOG2B) / kDeqRow : kHsDeqRows;
@@ -223,7 +228,8 @@ __device__ __forceinline__ void hadamard_dequant_finish(const DequantArgs& a, in
 #pragma unroll
   for (int r = 0; r < kHadamardRows; ++r)
     decode4<BITS>(word[r], (int)(lo % E) * BITS, f16_bits_to_f32(s16[r]), d[r]);
-  hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK>(d, hadamard_inverse_scale<LOG2B>());
+  hadamard_rows<kHadamardRows, 4, LANES, ROWS_PER_BLOCK, kHsDeqDpp>(d,
+                                                                    hadamard_inverse_scale<LOG2B>());
   // a partial last block is decompressed untransformed: its lanes decode
   // their values again (only a trip that reaches past the whole blocks)
   if ((base + kHadamardRows) * kDeqRow > nfull) {
@@ -243,12 +249,12 @@ __device__ __forceinline__ void hadamard_dequant_finish(const DequantArgs& a, in
 }
 
 template <int BITS, int LOG2B>
-__global__ __launch_bounds__(kDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
+__global__ __launch_bounds__(kHsDeqThreads) void hadamard_dequant_kernel(DequantArgs a) {
   constexpr int B = 1 << LOG2B;
   constexpr int R = hadamard_rows_per_trip<LOG2B>();
   static_assert(B <= R * kDeqRow, "a block must fit in one trip");
-  const int64_t wave = global_wave_id<kDeqThreads>();
-  const int64_t nwaves = (int64_t)gridDim.x * (kDeqThreads / kWave);
+  const int64_t wave = global_wave_id<kHsDeqThreads>();
+  const int64_t nwaves = (int64_t)gridDim.x * (kHsDeqThreads / kWave);
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   const int64_t ntrips = (nrows + R - 1) / R;
   for_each_trip(wave, ntrips, nwaves, [&](int64_t t) __attribute__((always_inline)) {

@@ -18,36 +18,55 @@
 namespace lowbit {
 
 // v[lane ^ D], D = 1 .. 32: ds_swizzle in bit-mask mode (and 0x1F, xor D)
-// within each half-wave, ds_bpermute across the halves
-template <int D>
+// within each half-wave, ds_bpermute across the halves.  DPP: partners 1, 2
+// and 8 apart by DPP moves instead (quad_perm, and row_ror:8, which within a
+// row of 16 lanes is lane ^ 8), and 16 apart by v_permlane16_swap (in
+// lane_butterfly): vector-ALU moves in place of LDS-pipe swizzles, which pays
+// where the vector ALU has room (the 4-bit B128 decompress of 64 Mi
+// elements: 58.2 -> 54.8 us) and not where it is the bound (the stochastic
+// compress: 8 % slower).  Partners 4 apart stay on ds_swizzle (two DPP row
+// shifts under bank masks measured 1 us slower).
+template <int D, bool DPP>
 __device__ __forceinline__ float xor_lane(float v) {
-  // (ds_swizzle uses the LDS pipe and leaves the vector ALU to the
-  // butterflies: DPP moves for partners 1 and 2 apart measured 8 % slower on
-  // the stochastic compress)
-  if constexpr (D <= 16) return swizzle_f32<0x1F | (D << 10)>(v);
+  if constexpr (DPP && D == 1) return dpp_f32<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (DPP && D == 2) return dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (DPP && D == 8) return dpp_f32<0x128>(v);  // row_ror:8
+  else if constexpr (D <= 16) return swizzle_f32<0x1F | (D << 10)>(v);
   else return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, __float_as_int(v)));
 }
 
 // One cross-lane stage (partners D lanes apart) on the N values of the lane.
-template <int D, int N>
+template <int D, int N, bool DPP>
 __device__ __forceinline__ void lane_butterfly(float* v) {
   const float sg = (lane_id() & D) ? -1.0f : 1.0f;
+  if constexpr (DPP && D == 16) {
+    // v_permlane16_swap of the value with itself: every lane receives the
+    // lower row's value (a) and the upper row's (b) of its pair of rows;
+    // a + b in the lower row, a - b in the upper one, as fma(b, +-1, a)
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const float p = xor_lane<D>(v[j]);
-    v[j] = __builtin_fmaf(v[j], sg, p);
+    for (int j = 0; j < N; ++j) {
+      const auto ab = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]),
+                                                       __float_as_uint(v[j]), false, false);
+      v[j] = __builtin_fmaf(__uint_as_float(ab[1]), sg, __uint_as_float(ab[0]));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float p = xor_lane<D, DPP>(v[j]);
+      v[j] = __builtin_fmaf(v[j], sg, p);
+    }
   }
 }
 
 // All cross-lane stages for blocks of LANES consecutive lanes (LANES <= 64).
-template <int LANES, int N>
+template <int LANES, int N, bool DPP>
 __device__ __forceinline__ void lane_stages(float* v) {
-  if constexpr (LANES > 1) lane_butterfly<1, N>(v);
-  if constexpr (LANES > 2) lane_butterfly<2, N>(v);
-  if constexpr (LANES > 4) lane_butterfly<4, N>(v);
-  if constexpr (LANES > 8) lane_butterfly<8, N>(v);
-  if constexpr (LANES > 16) lane_butterfly<16, N>(v);
-  if constexpr (LANES > 32) lane_butterfly<32, N>(v);
+  if constexpr (LANES > 1) lane_butterfly<1, N, DPP>(v);
+  if constexpr (LANES > 2) lane_butterfly<2, N, DPP>(v);
+  if constexpr (LANES > 4) lane_butterfly<4, N, DPP>(v);
+  if constexpr (LANES > 8) lane_butterfly<8, N, DPP>(v);
+  if constexpr (LANES > 16) lane_butterfly<16, N, DPP>(v);
+  if constexpr (LANES > 32) lane_butterfly<32, N, DPP>(v);
 }
 
 // Transform blocks laid out as v[row][elem] per lane: block-local index
@@ -55,7 +74,7 @@ __device__ __forceinline__ void lane_stages(float* v) {
 // N values per lane are contiguous, LANES lanes per row of the block
 // (a power of two <= 64) and the block spans ROWS_PER_BLOCK rows.  Then
 // multiply by the exact power of two `scale`.
-template <int ROWS, int N, int LANES, int ROWS_PER_BLOCK>
+template <int ROWS, int N, int LANES, int ROWS_PER_BLOCK, bool DPP = false>
 __device__ __forceinline__ void hadamard_rows(float (&v)[ROWS][N], float scale) {
   // strides 1 .. N/2: within the lane
 #pragma unroll
@@ -71,7 +90,7 @@ __device__ __forceinline__ void hadamard_rows(float (&v)[ROWS][N], float scale) 
         }
   // strides N .. N*LANES/2: across lanes
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) lane_stages<LANES, N>(v[r]);
+  for (int r = 0; r < ROWS; ++r) lane_stages<LANES, N, DPP>(v[r]);
   // larger strides: across the rows of the block
 #pragma unroll
   for (int m = 1; m < ROWS_PER_BLOCK; m <<= 1)
