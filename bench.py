@@ -140,19 +140,25 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when there is none for the current sources."""
+def read_traffic(kernel: str, workload: str = None):
+    """HBM bytes per launch of `kernel` from the committed counter summaries
+    (the line measured on `workload` when there is one, else any line of that
+    kernel), or None when there is none for the current sources."""
     digest = source_digest()
+    other = None
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             if not line.startswith("traffic:"):
                 continue
-            f = dict(kv.split("=", 1) for kv in line[len("traffic:"):].strip().split(" | ")[1:])
-            name = line[len("traffic:"):].strip().split(" | ")[0]
-            if name == kernel and f.get("source") == digest:
+            parts = line[len("traffic:"):].strip().split(" | ")
+            f = dict(kv.split("=", 1) for kv in parts[1:])
+            if parts[0] != kernel or f.get("source") != digest:
+                continue
+            if workload is not None and f.get("workload") == workload:
                 return float(f["bytes_per_launch"])
-    return None
+            if other is None:
+                other = float(f["bytes_per_launch"])
+    return other
 
 
 def main() -> int:
@@ -425,7 +431,7 @@ def main() -> int:
     del flush
 
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(kname)
+    traffic = read_traffic(kname, "step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname, "stage": name,
@@ -445,7 +451,7 @@ def main() -> int:
             return N * 2
         return N * 4
 
-    kernels = {s[0]: {"us": round(per_stage[i] * 1e3, 2),
+    kernels = {s[0]: {"us": round(per_stage[i] * 1e3, 2), "kernel": s[1], "alg_bytes": s[2],
                       "alg_GBps": round(s[2] / (per_stage[i] * 1e-3) / 1e9, 1),
                       "frac": round(s[2] / (per_stage[i] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
                       "input_GBps": round(input_bytes(s[0]) / (per_stage[i] * 1e-3) / 1e9, 1)}
@@ -493,6 +499,8 @@ def main() -> int:
                         "compress+apply (64Mi bf16, b4 B64)",
             "elements": N, "block_size": BLOCK, "bitwidths": list(BITS), "peers": PEERS,
             "value_counts": "binary32-equivalent bytes of the 15 stage passes / step time",
+            "step_alg_GBps": round(sum(st[2] for st in stages) / (ms_per_step * 1e-3) / 1e9, 1),
+            "step_alg_bytes": int(sum(st[2] for st in stages)),
             "schedule": f"{'+'.join(SCHEDULE[0])} alone on the main stream, then "
                         f"{'+'.join(SCHEDULE[1])} on the main stream concurrently with "
                         f"{'+'.join(SCHEDULE[2])} on a second stream, joined per step",
@@ -582,7 +590,7 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20, want=None):
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
                      "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3),
-                     "kernel": kernel, "traffic": read_traffic(kernel)}
+                     "kernel": kernel, "traffic": read_traffic(kernel, name)}
 
     # EF21 compress of the bucket (b4 B256 SR), state carried in place
     state = torch.zeros(N, dtype=torch.float32, device=dev)
@@ -688,6 +696,10 @@ def measure_compress_pattern(L, dev, x, reps=20):
         cg, dg, rg = (alg / (cms * 1e-3) / 1e9, alg / (dms * 1e-3) / 1e9,
                       ref / (rms * 1e-3) / 1e9)
         out[f"b{b}"] = {"workload": f"{N} fp32 bucket, b{b} B{BLOCK}" + (" SR" if b > 1 else ""),
+                        "alg_bytes": alg,
+                        "kernel": kname_quant(b, 8, b > 1, 0, 0, stream=True),
+                        "decompress_kernel": kname_dequant(b, 0, 0),
+                        "reference_kernel": kname_fold(b), "reference_bytes": ref,
                         "compress_us": round(cms * 1e3, 2), "compress_GBps": round(cg, 1),
                         "frac": round(cg / HBM_PEAK_GBS, 3),
                         "decompress_us": round(dms * 1e3, 2), "decompress_GBps": round(dg, 1),
@@ -730,7 +742,7 @@ def measure_configs(L, dev, reps=20, want=None):
         out[name] = {"workload": workload, "us": round(ms * 1e3, 2), "alg_bytes": int(alg_bytes),
                      "alg_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3),
                      "input_GBps": round(input_bytes / (ms * 1e-3) / 1e9, 1),
-                     "kernel": kernel, "traffic": read_traffic(kernel)}
+                     "kernel": kernel, "traffic": read_traffic(kernel, name)}
 
     # error feedback on 128 Mi bfloat16 gradients, b4 B128 SR
     n = 128 << 20

@@ -22,9 +22,15 @@ static lowbit_status launch_sign(const QuantArgs& a, bool stream_input, hipStrea
   lowbit_status st = LOWBIT_OK;
   if (full_tiles > 0) {
     const int64_t grid = grid_for_tiles(full_tiles);
-    if (stream_capable<MODE, DT, 4, 1>() && stream_input)
-      st = launch(&sign_kernel<LOG2B, DT, MODE, false, true>, grid, kBlockThreads, s, a, full_tiles);
-    else
+    bool streamed = false;
+    if constexpr (stream_capable<MODE, DT, 4, 1>()) {
+      if (stream_input) {
+        st = launch(&sign_kernel<LOG2B, DT, MODE, false, true>, grid, kBlockThreads, s, a,
+                    full_tiles);
+        streamed = true;
+      }
+    }
+    if (!streamed)
       st = launch(&sign_kernel<LOG2B, DT, MODE, false>, grid, kBlockThreads, s, a, full_tiles);
   }
   if (st == LOWBIT_OK && full_tiles * S::TILE < a.n)
@@ -70,10 +76,15 @@ static lowbit_status launch_q(const QuantArgs& a, bool stream_input, hipStream_t
     lowbit_status st = LOWBIT_OK;
     if (ntrips > 0) {
       const int64_t grid = grid_for_tiles(ntrips);
-      if (stream_capable<MODE, DT, S::E, S::R>() && stream_input)
-        st = launch(&quantize_kernel<BITS, LOG2B, SR, DT, MODE, false, true>, grid, kBlockThreads,
-                    s, a, full_tiles);
-      else
+      bool streamed = false;
+      if constexpr (stream_capable<MODE, DT, S::E, S::R>()) {
+        if (stream_input) {
+          st = launch(&quantize_kernel<BITS, LOG2B, SR, DT, MODE, false, true>, grid,
+                      kBlockThreads, s, a, full_tiles);
+          streamed = true;
+        }
+      }
+      if (!streamed)
         st = launch(&quantize_kernel<BITS, LOG2B, SR, DT, MODE, false>, grid, kBlockThreads, s, a,
                     full_tiles);
     }
