@@ -366,32 +366,15 @@ __device__ __forceinline__ float pow2_f32(int x) { return __uint_as_float((uint3
 // Loads and peer sums of one trip of NT full tiles for exactly eight peers
 // (exact_path): acc as decode_peer_group leaves it, i.e. 2^acc_shift<BITS>()
 // times the peer-ordered binary32 sums.
-template <int BITS, int LOG2B, int NT, bool STREAM>
-__device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t* wt,
-                                             const int64_t* kt, const uint32_t* wl,
-                                             const uint32_t* kl, float (*acc)[Grid<BITS>::E]) {
-  using S = TileShape<BITS, LOG2B>;
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  constexpr int E = S::E, R = S::R, W = NT * R;
-  constexpr int K = acc_shift<BITS>();
-  constexpr uint32_t HALF = Grid<BITS>::HALF;
-  const int p = lane_id() & 7;        // the peer whose scale this lane loads
-  // the code words of all eight peers (pointers read in one batch)
-  const uint32_t* cps[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) cps[q] = a.codes[q];
-  uint32_t w[8][W][1];
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[q][i][0] = load_once<STREAM>(cps[q] + wt[i / R] + wl[i]);
-  // one scale per lane and slot: peer p's scale of the lane's block (a block
-  // spans at least 8 lanes, so each aligned group of 8 lanes holds all eight).
-  // The eight pointers are made wave-uniform first, so that they are read
-  // with the scalar loads of the argument block and selected per lane in
-  // registers; a per-lane choice among argument-block slots would otherwise
-  // become a vector load of the pointer, which the code word loads then wait
-  // behind.
+// The scale array of peer p = lane & 7, the peer whose scales this lane
+// loads (a block spans at least 8 lanes, so each aligned group of 8 lanes
+// holds all eight).  The eight pointers are made wave-uniform first, so that
+// they are read with the scalar loads of the argument block and selected per
+// lane in registers; a per-lane choice among argument-block slots would
+// otherwise become a vector load of the pointer, which the code word loads
+// then wait behind.
+__device__ __forceinline__ global_ptr<uint16_t> peer_scale_ptr(const ReduceArgs& a) {
+  const int p = lane_id() & 7;
   global_ptr<uint16_t> sq[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) sq[q] = uniform_ptr(a.scales[q]);
@@ -401,10 +384,42 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
   const global_ptr<uint16_t> s67 = (p & 1) ? sq[7] : sq[6];
   const global_ptr<uint16_t> s03 = (p & 2) ? s23 : s01;
   const global_ptr<uint16_t> s47 = (p & 2) ? s67 : s45;
-  const global_ptr<uint16_t> sp = (p & 4) ? s47 : s03;
-  uint32_t s16[W];
+  return (p & 4) ? s47 : s03;
+}
+
+// Loads of one trip of NT full tiles for exactly eight peers: the code words
+// of every peer and slot, and per slot the scale of peer lane & 7 (sp).
+template <int BITS, int LOG2B, int NT, bool STREAM>
+__device__ __forceinline__ void reduce8_load(
+    const ReduceArgs& a, global_ptr<uint16_t> sp, const int64_t* wt, const int64_t* kt,
+    const uint32_t* wl, const uint32_t* kl,
+    uint32_t (*w)[TileShape<BITS, LOG2B>::R * NT][1], uint32_t* s16) {
+  using S = TileShape<BITS, LOG2B>;
+  constexpr int R = S::R, W = NT * R;
+  // the code words of all eight peers (pointers read in one batch)
+  const uint32_t* cps[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) cps[q] = a.codes[q];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[q][i][0] = load_once<STREAM>(cps[q] + wt[i / R] + wl[i]);
 #pragma unroll
   for (int i = 0; i < W; ++i) s16[i] = (sp + kt[i / R])[kl[i]];
+}
+
+// Peer sums of a loaded trip (reduce8_load): acc as decode_peer_group leaves
+// it, i.e. 2^acc_shift<BITS>() times the peer-ordered binary32 sums.
+template <int BITS, int LOG2B, int NT>
+__device__ __forceinline__ void reduce8_sums_loaded(
+    const ReduceArgs& a, const uint32_t (*w)[TileShape<BITS, LOG2B>::R * NT][1],
+    const uint32_t* s16, float (*acc)[Grid<BITS>::E]) {
+  using S = TileShape<BITS, LOG2B>;
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  constexpr int E = S::E, R = S::R, W = NT * R;
+  constexpr int K = acc_shift<BITS>();
+  constexpr uint32_t HALF = Grid<BITS>::HALF;
+  (void)R;
   // per slot: exponent range of the group's nonzero scales
   uint32_t lo[W];
   bool ok = true;
@@ -490,6 +505,18 @@ __device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t*
   }
 }
 
+// Loads and peer sums of one trip of NT full tiles for exactly eight peers
+// (exact_path).
+template <int BITS, int LOG2B, int NT, bool STREAM>
+__device__ __forceinline__ void reduce8_sums(const ReduceArgs& a, const int64_t* wt,
+                                             const int64_t* kt, const uint32_t* wl,
+                                             const uint32_t* kl, float (*acc)[Grid<BITS>::E]) {
+  constexpr int W = NT * TileShape<BITS, LOG2B>::R;
+  uint32_t w[8][W][1], s16[W];
+  reduce8_load<BITS, LOG2B, NT, STREAM>(a, peer_scale_ptr(a), wt, kt, wl, kl, w, s16);
+  reduce8_sums_loaded<BITS, LOG2B, NT>(a, w, s16, acc);
+}
+
 // Reduce and requantize NT consecutive output tiles starting at tile `tile0`,
 // any number of peers (groups of G: all loads of a group are issued before
 // any of its peers is decoded; NPC > 0: exactly NPC peers).  GUARD: the tiles
@@ -555,7 +582,10 @@ __global__ __launch_bounds__(kBlockThreads) void reduce_kernel(ReduceArgs a, int
     // eight peers (one per GPU of an 8-GPU node): the straight-line form.
     // The grid gives every wave one trip; the loop only runs where the grid
     // was capped (more than 2^32 work-items), so the first trip is kept out
-    // of it and its addresses are not carried from trip to trip.
+    // of it and its addresses are not carried from trip to trip.  (Waves
+    // that take two trips and issue the second trip's loads before the first
+    // trip's sums measured no faster: 8 x 32 Mi b4 in one receive buffer
+    // 33.6 against 31.9 us.)
     if (a.npeers == 8) {
       if (trip < ntrips)
         reduce_tiles<IN_BITS, BITS, LOG2B, SR, EF, U, false, 8, STREAM>(a, trip * U);
