@@ -10,11 +10,14 @@
 namespace lowbit {
 
 // 4-bit same-width reduce in the row layout when a binary32 stream is part
-// of it (the stage-2 residual or the sum output): measured on 8 x 32 Mi
-// peers, b4 B128, with residual 83 -> 75 us, with the sum 65 -> 57 us.  The
-// plain reduce keeps the general tile (40 -> 49 us in the row layout, where
-// two lanes load each code word and every lane its scale; at 2 bits
-// 33 -> 58 us).
+// of it (the stage-2 residual or the sum output) and blocks are at most 1024
+// elements.  8 x 32 Mi peers, row layout against the general tile, with the
+// residual / with the sum: B128 68.6 / 56.0 against 77.4 / 68.2 us, B512
+// 67.7 / 54.7 against 78.3 / 67.6, B1024 67.2 / 53.2 against 76.8 / 62.7,
+// B2048 101 / 65 against 74 / 62, B4096 163 / 99 against 84 / 77 (a trip of
+// B/256 rows holds few peers' loads in flight).  The plain reduce keeps the
+// general tile (40 -> 49 us in the row layout, where two lanes load each
+// code word and every lane its scale; at 2 bits 33 -> 58 us).
 template <int BITS, int LOG2B, bool SR, bool EF>
 static lowbit_status launch_rr(bool stream_input, const ReduceArgs& a, hipStream_t s) {
   using S = RowrShape<BITS, LOG2B, EF>;
@@ -41,7 +44,7 @@ static lowbit_status launch_rr(bool stream_input, const ReduceArgs& a, hipStream
 // streaming reduces.)
 template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF>
 static lowbit_status launch_r(bool stream_input, const ReduceArgs& a, hipStream_t s) {
-  if constexpr (IN_BITS == BITS && BITS == 4) {
+  if constexpr (IN_BITS == BITS && BITS == 4 && LOG2B <= 10) {
     if (EF || a.out_sum) return launch_rr<BITS, LOG2B, SR, EF>(stream_input, a, s);
   }
   {
