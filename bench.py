@@ -85,12 +85,8 @@ METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HB
 # demangled kernel names as rocprofv3 reports them
 def kname_quant(bits, log2b, sr, dt, mode, tail=False, stream=False):
     """stream: the non-temporal-input form, taken by a plain binary32 compress
-    without LOWBIT_HINT_INPUT_REUSED where a lane's elements of a block lie in
-    one row of code words (4 codes per word, or blocks of at most 64 words)."""
-    e = 32 // bits
-    rows = max(1, (1 << log2b) // (64 * e)) if bits > 1 else 1
-    ntx = str(bool(stream) and mode == 0 and dt == 0 and (e == 4 or rows == 1)
-              and not tail).lower()
+    without LOWBIT_HINT_INPUT_REUSED."""
+    ntx = str(bool(stream) and mode == 0 and dt == 0 and not tail).lower()
     if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
         return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}, {ntx}>" \
                f"(lowbit::QuantArgs, long)"

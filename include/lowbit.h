@@ -96,8 +96,7 @@ typedef enum {
  * peers' codes after reducing them): keep it in the caches.  Without it the
  * input is streamed where the access pattern allows (non-temporal loads), which
  * is faster for data read once: the binary32 input of the plain compress
- * (lowbit_quantize_pack: at 1 and 8 bits, and at 2 and 4 bits when a block
- * spans at most 64 code words) and the peers' code words of the local reduce
+ * (lowbit_quantize_pack) and the peers' code words of the local reduce
  * (taken from in_p of lowbit_reduce_requant and lowbit_reduce_requant_ef).
  * Accepted by every entry point; the others ignore it. */
 #define LOWBIT_HINT_INPUT_REUSED 1

@@ -51,7 +51,7 @@ def _device():
 @pytest.mark.parametrize("bits", BITS)
 def test_quantize_input_reused_hint(bits, B, sr):
     """LOWBIT_HINT_INPUT_REUSED selects cached rather than streamed loads of
-    the binary32 input (where the tile shape streams it); the codes and scales
+    the binary32 input of every plain compress; the codes and scales
     are the same."""
     for i, n in enumerate(_sizes(bits, B)):
         x = _input("mixed", n, 7000 * bits + B + i, "f32")

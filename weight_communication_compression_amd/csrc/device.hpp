@@ -313,20 +313,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // A plain compress of binary32 input reads it as a stream (non-temporal
 // loads) unless the caller says it reads the input again soon
-// (LOWBIT_HINT_INPUT_REUSED), wherever a wave's 16-byte loads cover
-// consecutive 16-byte pieces: the 1-bit compress, the 8-bit one (four
-// elements per lane, R rows of them) and the 2- and 4-bit ones whose tile is
-// one row (read through LDS, see load_tile_staged).  Measured on the 64 Mi bucket, each alone after the
-// Infinity Cache was cleared: 1 bit 50.6 -> 46.3 us, 8 bits 61.6 -> 59.1 us;
-// but a second compress of the same bucket right after one with
-// non-temporal loads finds none of it in the Infinity Cache (2-bit compress
-// 49 -> 57 us).  Where a lane's elements span several 16-byte pieces (2 and 4
-// bits: 64- and 32-byte lane strides) the hint costs up to 50 % (each load
-// instruction then fetches half lines that the next one refetches) and is
-// never applied.
+// (LOWBIT_HINT_INPUT_REUSED).  Every such compress reads its input with
+// loads whose 16-byte pieces are consecutive across the wave: the 1-bit
+// compress (four elements per lane), the 8-bit one (four elements per lane,
+// R rows of them) and the 2- and 4-bit ones through LDS (load_tile_staged).
+// Measured on the 64 Mi bucket, each alone after the Infinity Cache was
+// cleared: 1 bit 50.6 -> 46.3 us, 8 bits 61.6 -> 59.1 us; but a second
+// compress of the same bucket right after one with non-temporal loads finds
+// none of it in the Infinity Cache (2-bit compress 49 -> 57 us).  (With a
+// lane's own 32- or 64-byte span loaded directly, non-temporal loads cost up
+// to 50 %: each load instruction then fetches half lines that the next one
+// refetches.)
 template <int MODE, int DT, int E, int R>
 constexpr bool stream_capable() {
-  return MODE == kPlain && DT == kF32 && (E == 4 || R == 1);
+  return MODE == kPlain && DT == kF32 && E >= 4 && R >= 1;
 }
 
 // Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8

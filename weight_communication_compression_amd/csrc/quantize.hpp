@@ -174,34 +174,45 @@ __device__ __forceinline__ void quantize_tile(
 // instruction one contiguous kilobyte) -- non-temporal when streamed --,
 // writes them to its own LDS slice and reads back its E consecutive elements.
 // A wave's LDS accesses execute in order, so no barrier is needed; the wave
-// barrier keeps the compiler from moving the reads above the writes.  (One
-// tile per trip whenever E > 4 for this mode, so one slice per wave.)
+// barriers keep the compiler from moving the reads above the writes, or a
+// row's writes above the previous row's reads (the R rows of a tile pass
+// through the wave's one slice in turn, after all their global loads have
+// been issued).
 template <int MODE, int DT, int E, int R>
 constexpr bool staged_tile() {
-  return MODE == kPlain && DT == kF32 && E > 4 && R == 1;
+  return MODE == kPlain && DT == kF32 && E > 4;
 }
 
-template <int E, bool NT>
-__device__ __forceinline__ void load_tile_staged(const float* x, int64_t t0, float* v) {
+// The R rows of 64 words of the tile at element t0.
+template <int E, int R, bool NT>
+__device__ __forceinline__ void load_tile_staged(const float* x, int64_t t0, float (&v)[R][E]) {
   constexpr int Q = E / 4;                               // 16-byte pieces per lane
   __shared__ f32x4 stage[kBlockThreads / kWave][kWave * Q];
   f32x4* st = stage[threadIdx.x >> 6];
   const int lane = lane_id();
   const f32x4* src = reinterpret_cast<const f32x4*>(x + t0);
-  f32x4 t[Q];
+  f32x4 t[R][Q];
 #pragma unroll
-  for (int k = 0; k < Q; ++k)
-    t[k] = NT ? __builtin_nontemporal_load(src + k * kWave + lane) : src[k * kWave + lane];
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-  for (int k = 0; k < Q; ++k) st[k * kWave + lane] = t[k];
-  __builtin_amdgcn_wave_barrier();
+    for (int k = 0; k < Q; ++k) {
+      const f32x4* p = src + (r * Q + k) * kWave + lane;
+      t[r][k] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
 #pragma unroll
-  for (int j = 0; j < Q; ++j) {
-    const f32x4 u = st[lane * Q + j];
-    v[4 * j + 0] = u.x;
-    v[4 * j + 1] = u.y;
-    v[4 * j + 2] = u.z;
-    v[4 * j + 3] = u.w;
+  for (int r = 0; r < R; ++r) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < Q; ++k) st[k * kWave + lane] = t[r][k];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const f32x4 u = st[lane * Q + j];
+      v[r][4 * j + 0] = u.x;
+      v[r][4 * j + 1] = u.y;
+      v[r][4 * j + 2] = u.z;
+      v[r][4 * j + 3] = u.w;
+    }
   }
 }
 
@@ -214,13 +225,17 @@ __device__ __forceinline__ void load_tile(const QuantArgs& a, int64_t t0,
   using S = TileShape<BITS, LOG2B>;
   constexpr int E = S::E, R = S::R;
   const int lane = lane_id();
+  if constexpr (FULL && staged_tile<MODE, DT, E, R>()) {
+    // the plain mode: x alone
+    load_tile_staged<E, R, NTX>(static_cast<const float*>(a.x), t0, v);
+    (void)h;
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t off = (uint32_t)(r * kWave + lane) * E;
     float w[E];
-    if constexpr (FULL && staged_tile<MODE, DT, E, R>()) {
-      load_tile_staged<E, NTX>(static_cast<const float*>(a.x), t0, v[r]);
-    } else if constexpr (FULL) {
+    if constexpr (FULL) {
       constexpr bool RMW = MODE == kErrorFeedback || MODE == kEF21;
       load_vec<DT, E, NTX && E == 4 && stream_capable<MODE, DT, E, R>()>(a.x, t0, off, v[r]);
       if constexpr (RMW) load_vec<kF32, E>(a.resid, t0, off, w);
