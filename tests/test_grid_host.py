@@ -44,6 +44,7 @@ TRIPS = {
     "4-bit general tile, 2 tiles (1024 elements)": (1024, 256),
     "decompress, 2 rows of 256": (512, 128),
     "apply, 2 rows of 512": (1024, 128),
+    "Hadamard decompress B4096, a workgroup of 4 waves per block": (1024, 256),
 }
 
 

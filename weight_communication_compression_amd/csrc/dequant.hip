@@ -32,6 +32,24 @@ lowbit_status launch_dequant(int bits, bool apply, int dt, const DequantArgs& a,
 
 template <int BITS, int LOG2B>
 static lowbit_status launch_hd(const DequantArgs& a, hipStream_t s) {
+  if constexpr (LOG2B == 12) {
+    // whole blocks: a workgroup each; a partial last block: the one-wave trip
+    // on the remainder (as a buffer of its own, which starts on a block)
+    const int64_t nfull = a.n >> LOG2B;
+    lowbit_status st = LOWBIT_OK;
+    if (nfull > 0)
+      st = launch(&hadamard_dequant_big_kernel<BITS>,
+                  grid_blocks(nfull * kHsBigWaves, kHsBigWaves * kWave), kHsBigWaves * kWave, s,
+                  a, nfull);
+    const int64_t done = nfull << LOG2B;
+    if (st != LOWBIT_OK || done == a.n) return st;
+    DequantArgs rest = a;
+    rest.codes = a.codes + done / Grid<BITS>::E;
+    rest.scales = a.scales + nfull;
+    rest.y = a.y + done;
+    rest.n = a.n - done;
+    return launch(&hadamard_dequant_kernel<BITS, LOG2B>, 1, kHsDeqThreads, s, rest);
+  }
   const int64_t nrows = (a.n + kDeqRow - 1) / kDeqRow;
   constexpr int ROWS = hadamard_rows_per_trip<LOG2B>();
   const int64_t waves = (nrows + ROWS - 1) / ROWS;   // one trip per wave

@@ -270,6 +270,72 @@ __global__ __launch_bounds__(kHsDeqThreads) void hadamard_dequant_kernel(Dequant
   });
 }
 
+// Decompress with the inverse transform for blocks of 4096 elements: one
+// workgroup of kHsBigWaves waves per block, each wave 4 rows of 256 (16
+// values per lane).  A wave transforms its 1024 elements in registers
+// (strides 1 .. 512: in the lane, across lanes, across its rows), then the
+// strides 1024 and 2048 pair the waves w and w ^ 1, then w and w ^ 2, through
+// LDS: every lane writes its 16 values, the workgroup synchronizes, and each
+// lane reads the values at the same position of the partner wave and keeps
+// fma(own, +-1, partner) as the lane exchanges do; then the scale, then the
+// stores.  The same binary32 operations in the same stage order as the
+// one-wave trip, which at this block size holds 64 values per lane (252
+// VGPRs, two waves per SIMD).  Whole blocks only: the caller decompresses a
+// partial last block with hadamard_dequant_kernel.  `nblocks` whole blocks;
+// a workgroup takes block blockIdx.x and, where the grid was capped, every
+// gridDim.x-th one after it (the whole workgroup alike, so that all its waves
+// reach each barrier).
+constexpr int kHsBigWaves = 4;
+template <int BITS>
+__device__ __forceinline__ void hadamard_dequant_big_block(const DequantArgs& a, int64_t blk);
+template <int BITS>
+__global__ __launch_bounds__(kHsBigWaves * kWave) void hadamard_dequant_big_kernel(DequantArgs a,
+                                                                                  int64_t nblocks) {
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x)   // workgroup-uniform
+    hadamard_dequant_big_block<BITS>(a, blk);
+}
+template <int BITS>
+__device__ __forceinline__ void hadamard_dequant_big_block(const DequantArgs& a, int64_t blk) {
+  constexpr int E = Grid<BITS>::E;
+  constexpr int RW = 4;                                   // rows per wave
+  constexpr int LOG2B = 12;
+  static_assert(kHsBigWaves * RW * kDeqRow == (1 << LOG2B), "one block per workgroup");
+  __shared__ float xch[kHsBigWaves][RW * 4][kWave];
+  const int wv = (int)(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const uint32_t lo = 4u * (uint32_t)lane;
+  const int64_t row0 = blk * (kHsBigWaves * RW) + wv * RW;   // the wave's first row
+  uint32_t word[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) word[r] = (a.codes + (row0 + r) * kDeqRow / E)[lo / E];
+  const float s = f16_bits_to_f32(a.scales[blk]);
+  float d[RW][4];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) decode4<BITS>(word[r], (int)(lo % E) * BITS, s, d[r]);
+  hadamard_rows<RW, 4, kWave, RW, kHsDeqDpp>(d, 1.0f);   // strides 1 .. 512 (x 1: exact)
+#pragma unroll
+  for (int m = 1; m < kHsBigWaves; m <<= 1) {             // strides 1024, 2048
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xch[wv][r * 4 + j][lane] = d[r][j];
+    __syncthreads();
+    const float sg = (wv & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[r][j] = __builtin_fmaf(d[r][j], sg, xch[wv ^ m][r * 4 + j][lane]);
+    __syncthreads();
+  }
+  constexpr float scale = hadamard_inverse_scale<LOG2B>();
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[r][j] = d[r][j] * scale;
+    store_vec_f32<4>(a.y, (row0 + r) * kDeqRow, lo, d[r]);
+  }
+}
+
 // Plain binary32 copy with the codec kernels' launch shape (measurement aid):
 // one float4 per thread and trip.
 __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const float* x, float* y, int64_t n) {
