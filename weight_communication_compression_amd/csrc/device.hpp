@@ -288,14 +288,46 @@ __device__ __forceinline__ BlockScale make_scale(float t) {
 }
 
 // ----------------------------------------------------------------- hash --
-// MurmurHash3 32-bit finaliser, and its steps after the first xor-shift.
-__device__ __forceinline__ uint32_t fmix32_after_first_step(uint32_t h) {
-  h *= 0x85EBCA6Bu;
+// MurmurHash3 32-bit finaliser, its steps after the first xor-shift, and
+// its steps after the first multiply.
+constexpr uint32_t kFmixK1 = 0x85EBCA6Bu;
+constexpr uint32_t kFmixK2 = 0xC2B2AE35u;
+__device__ __forceinline__ uint32_t fmix32_after_first_multiply(uint32_t h) {
   h ^= h >> 13;
-  h *= 0xC2B2AE35u;
+  h *= kFmixK2;
   h ^= h >> 16;
   return h;
 }
+__device__ __forceinline__ uint32_t fmix32_after_first_step(uint32_t h) {
+  return fmix32_after_first_multiply(h * kFmixK1);
+}
+
+// The first products (c ^ j) * K1 (mod 2^32) for j = 0 .. N - 1 (N a power
+// of two, at most 16) with one add or subtract each instead of a multiply.
+// Walking j in Gray-code order, j_k = k ^ (k >> 1), consecutive values differ
+// in one bit b; flipping bit b of c ^ j changes the product by +-K1 * 2^b,
+// plus when the bit becomes set.  d[b] = (1 - 2 c_b) K1 2^b is the change
+// when bit b of j goes from 0 to 1.
+template <int N>
+struct GrayProducts {
+  static constexpr int LOG2N = N <= 1 ? 0 : N <= 2 ? 1 : N <= 4 ? 2 : N <= 8 ? 3 : 4;
+  static_assert((1 << LOG2N) == N && N <= 16, "N a power of two up to 16");
+  uint32_t p;                       // the product for the current j
+  uint32_t d[LOG2N > 0 ? LOG2N : 1];
+  __device__ __forceinline__ explicit GrayProducts(uint32_t c) {
+    p = c * kFmixK1;                // j = 0
+#pragma unroll
+    for (int b = 0; b < LOG2N; ++b)
+      d[b] = ((c >> b) & 1u) ? 0u - (kFmixK1 << b) : (kFmixK1 << b);
+  }
+  // the j of step k, and the product for it (step k >= 1 follows step k - 1)
+  static constexpr int index(int k) { return k ^ (k >> 1); }
+  __device__ __forceinline__ void step(int k) {
+    const int flip = index(k) ^ index(k - 1);            // one bit
+    const int b = flip == 1 ? 0 : flip == 2 ? 1 : flip == 4 ? 2 : 3;
+    p = (index(k) & flip) ? p + d[b] : p - d[b];
+  }
+};
 __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return fmix32_after_first_step(h ^ (h >> 16));
 }

@@ -62,7 +62,12 @@ struct TileShape {
 // dequantized values.  K > 0 lets a caller hand over values it accumulated
 // scaled by 2^K: the statistic and the reciprocal absorb the exact factor, so
 // the codes are those of the unscaled values (no value here is subnormal).
-template <int BITS, int LOG2B, bool SR, bool WANT_DEQ, int K = 0>
+// GRAY: the first products of the SR hash by GrayProducts (one add per
+// element instead of a multiply, a few more instructions per word): the
+// Hadamard-smoothed compress, bound by the vector ALU, 58.4 -> 57.5 us (4-bit
+// B128, 64 Mi); the other compresses are faster with the multiplies (4-bit
+// B256 alone 49.6 -> 50.0 us).
+template <int BITS, int LOG2B, bool SR, bool WANT_DEQ, int K = 0, bool GRAY = false>
 __device__ __forceinline__ void quantize_tile(
     const float (&v)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E], int64_t t0, int64_t n,
     bool full, const TileOut& o, float (&deq)[TileShape<BITS, LOG2B>::R][Grid<BITS>::E]) {
@@ -129,18 +134,25 @@ __device__ __forceinline__ void quantize_tile(
       // (the low half of the first element's global index) is a multiple of
       // E, so lo + j = lo ^ j, and j < 2^16 leaves x >> 16 unchanged: the
       // first fmix32 step, x ^ (x >> 16), is c ^ j with c computed once.
+      // The word's elements go in Gray-code order, so that the first hash
+      // products can follow one another by an add (GrayProducts); the
+      // packing adds are exact, so the order does not change the word.
       uint32_t c = 0;
       if constexpr (SR) {
         const uint64_t gi = o.index_offset + (uint64_t)i0;
         const uint32_t x0 = (uint32_t)gi ^ fmix32((uint32_t)(gi >> 32) ^ o.key);
         c = x0 ^ (x0 >> 16);
       }
+      GrayProducts<E> gp(c);
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
+      for (int k = 0; k < E; ++k) {
+        const int j = GrayProducts<E>::index(k);
+        if (k > 0) gp.step(k);
         const float x = v[r][j] * inv;
         float q;
         if constexpr (SR) {
-          const uint32_t h = fmix32_after_first_step(c ^ (uint32_t)j);
+          const uint32_t h = GRAY ? fmix32_after_first_multiply(gp.p)
+                                  : fmix32_after_first_step(c ^ (uint32_t)j);
           // the random offset (h >> 8) * 2^-24 is exact, so the fused form
           // rounds once, exactly like adding it in binary32.
           const float y = __builtin_fmaf((float)(h >> 8), 0x1p-24f, x);
@@ -291,7 +303,7 @@ __device__ __forceinline__ void finish_tile(const QuantArgs& a, int64_t t0,
   constexpr bool WANT_DEQ = MODE == kErrorFeedback || MODE == kEF21;
   const int lane = lane_id();
   float deq[R][E];
-  quantize_tile<BITS, LOG2B, SR, WANT_DEQ>(v, t0, a.n, FULL, a.out, deq);
+  quantize_tile<BITS, LOG2B, SR, WANT_DEQ, 0, MODE == kHadamard>(v, t0, a.n, FULL, a.out, deq);
   if constexpr (WANT_DEQ) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
