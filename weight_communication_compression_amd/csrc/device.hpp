@@ -127,10 +127,12 @@ __device__ __forceinline__ void for_each_trip(int64_t first, int64_t count, int6
   for (int64_t i = first + stride; i < count; i += stride) body(i);
 }
 
+// DPP moves with every row and bank enabled; every control used here gives
+// each lane a source lane inside its row, so no lane keeps an old value and
+// none is supplied (mov_dpp: no move of a zero first).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 template <int PATTERN>
@@ -163,7 +165,7 @@ __device__ __forceinline__ float group_reduce(float v) {
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 // Maximum over aligned groups of L lanes of a non-negative binary32 value,
