@@ -568,20 +568,23 @@ __device__ __forceinline__ void reduce_tiles(const ReduceArgs& a, int64_t tile0)
 // Waves per SIMD the register allocation must allow (1: no bound) for the
 // same-width main kernels of blocks up to 1024 elements: measured on 8 x 32 Mi
 // peers, b4 B128, 84 VGPRs (5 waves) 32.1 us in one receive buffer, 68 VGPRs
-// (7 waves) 30.1 us, with no scratch.  The bound is chosen per width so that
-// no kernel spills (1 bit: 91 VGPRs, 5 waves; 2 bits: 57-60, 8 waves;
-// 4 bits: 67-71, 7 waves); the 8-bit kernels (94-114 VGPRs) would spill with
-// five.
-template <int IN_BITS, int BITS, int LOG2B, bool EF, bool TAIL>
+// (7 waves) 30.1 us, with no scratch; the step's 8-bit reduce of 8 Mi
+// shares (B256, nearest) 21.5 -> 20.8 us at 5 waves.  The bound is chosen per
+// kernel so that none spills (1 bit: 91 VGPRs, 5 waves; 2 bits: 57-60, 8
+// waves; 4 bits: 67-71, 7 waves; 8 bits with nearest rounding and blocks up
+// to 512: 96, 5 waves); the 8-bit stochastic-rounding kernels and the mixed
+// widths would spill (or measured no faster: 8 -> 4 bits at 6 waves).
+template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL>
 constexpr int reduce_min_waves() {
-  if (TAIL || EF || IN_BITS != BITS || LOG2B > 10 || BITS == 8) return 1;
+  if (TAIL || EF || LOG2B > 10 || IN_BITS != BITS) return 1;
+  if (BITS == 8) return (!SR && LOG2B <= 9) ? 5 : 1;
   return BITS == 2 ? 8 : BITS == 4 ? 7 : 5;
 }
 
 // STREAM: the peers' code words are read non-temporally (main kernel only).
 template <int IN_BITS, int BITS, int LOG2B, bool SR, bool EF, bool TAIL, bool STREAM = false>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((
-    amdgpu_waves_per_eu(reduce_min_waves<IN_BITS, BITS, LOG2B, EF, TAIL>()))) void
+    amdgpu_waves_per_eu(reduce_min_waves<IN_BITS, BITS, LOG2B, SR, EF, TAIL>()))) void
 reduce_kernel(ReduceArgs a, int64_t first) {
   using S = TileShape<BITS, LOG2B>;
   constexpr int U = reduce_tiles_per_trip<S::R * S::E>();
