@@ -84,9 +84,9 @@ METRIC = "quantize+pack / reduce-requant GB/s of fp32 input on 1 MI355X; % of HB
 
 # demangled kernel names as rocprofv3 reports them
 def kname_quant(bits, log2b, sr, dt, mode, tail=False, stream=False):
-    """stream: the non-temporal-input form, taken by a plain binary32 compress
-    without LOWBIT_HINT_INPUT_REUSED."""
-    ntx = str(bool(stream) and mode == 0 and dt == 0 and not tail).lower()
+    """stream: the non-temporal-input form, taken by a plain or Hadamard-smoothed
+    binary32 compress without LOWBIT_HINT_INPUT_REUSED."""
+    ntx = str(bool(stream) and mode in (0, 4) and dt == 0 and not tail).lower()
     if bits == 1 and mode != 4:     # 1-bit compress: the coalesced sign kernel
         return f"void lowbit::sign_kernel<{log2b}, {dt}, {mode}, {str(tail).lower()}, {ntx}>" \
                f"(lowbit::QuantArgs, long)"
@@ -611,7 +611,7 @@ def measure_next_rows(L, lib, dev, stream, x, reps=20, want=None):
     timed("hadamard_quantize_pack b4", f"{N} fp32 bucket, b4 B{HB} SR", hb,
           lib.lowbit_hadamard_quantize_pack,
           (P(x.data_ptr()), L.F32, N, ctypes.byref(qh), P(c.data_ptr()), P(s.data_ptr()), sh),
-          kname_quant(4, 7, True, 0, 4))
+          kname_quant(4, 7, True, 0, 4, stream=True))
     timed("hadamard_unpack_dequant b4", f"{N} elements, b4 B{HB}", hb,
           lib.lowbit_hadamard_unpack_dequant,
           (P(c.data_ptr()), P(s.data_ptr()), N, ctypes.byref(qh), P(yh.data_ptr()), sh),

@@ -95,8 +95,9 @@ typedef enum {
  * it compresses the same buffer at another bitwidth next, or decompresses the
  * peers' codes after reducing them): keep it in the caches.  Without it the
  * input is streamed where the access pattern allows (non-temporal loads), which
- * is faster for data read once: the binary32 input of the plain compress
- * (lowbit_quantize_pack) and the peers' code words of the local reduce
+ * is faster for data read once: the binary32 input of the plain and the
+ * Hadamard-smoothed compress (lowbit_quantize_pack,
+ * lowbit_hadamard_quantize_pack) and the peers' code words of the local reduce
  * (taken from in_p of lowbit_reduce_requant and lowbit_reduce_requant_ef).
  * Accepted by every entry point; the others ignore it. */
 #define LOWBIT_HINT_INPUT_REUSED 1

@@ -40,7 +40,7 @@ def bench_kernel_names():
                   bench.kname_dequant(b, 0, 0),
                   bench.kname_fold(b)]
     names += [bench.kname_quant(4, 8, True, 0, 3),          # EF21
-              bench.kname_quant(4, 7, True, 0, 4),          # Hadamard compress
+              bench.kname_quant(4, 7, True, 0, 4, stream=True),   # Hadamard compress
               bench.kname_hadamard_dequant(4, 7),
               bench.kname_reduce(4, 4, 7, False, True),     # stage-2 EF reduce (row layout)
               bench.kname_reduce(8, 4, 7, False),           # 8-bit -> 4-bit reduce

@@ -201,6 +201,26 @@ def test_hadamard_compress_decompress(bits, B, sr, dtype):
         assert_same(f32_np(y), O.hadamard_unpack_dequant(wc, ws, n, bits, B), f"values n={n}")
 
 
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("B", [32, 128, 4096])
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_hadamard_compress_input_reused_hint(bits, B, sr):
+    """Streamed (default) and cached (LOWBIT_HINT_INPUT_REUSED) loads of the
+    binary32 input give the same codes and scales."""
+    T = _tile(bits, B)
+    for i, n in enumerate([9 * T, 4 * T + B + 37]):
+        x = np.random.default_rng(50 + i).standard_t(3, n).astype(np.float32)
+        say(f"hadamard compress (input reused) bits={bits} B={B} sr={sr} n={n}")
+        gx = to_gpu(x)
+        c, s = L.hadamard_quantize_pack(gx, bits, B, sr, 21, 0, input_reused=True)
+        c2, s2 = L.hadamard_quantize_pack(gx, bits, B, sr, 21, 0)
+        torch.cuda.synchronize()
+        wc, ws = O.hadamard_quantize_pack(x, bits, B, sr, 21, 0)
+        for cc, ss in ((c, s), (c2, s2)):
+            assert_same(scales_np(ss), ws, f"scales n={n}")
+            assert_same(codes_np(cc), wc, f"codes n={n}")
+
+
 def test_hadamard_size_rules_raise():
     x = torch.zeros(200, device="cuda")
     for B in (16, 96, 8192):

@@ -127,7 +127,8 @@ lowbit_status lowbit_hadamard_quantize_pack(const void* x, lowbit_dtype xt, int6
   a.x = x;
   a.n = n;
   a.out = TileOut{codes, scales, p->index_offset, seed_key(p->seed)};
-  return launch_quantize_hadamard(p->bitwidth, lb, p->stochastic != 0, (int)xt, false, a, stream);
+  return launch_quantize_hadamard(p->bitwidth, lb, p->stochastic != 0, (int)xt,
+                                  (p->hints & LOWBIT_HINT_INPUT_REUSED) == 0, a, stream);
 }
 
 lowbit_status lowbit_hadamard_unpack_dequant(const uint32_t* codes, const uint16_t* scales,

@@ -360,7 +360,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // refetches.)
 template <int MODE, int DT, int E, int R>
 constexpr bool stream_capable() {
-  return MODE == kPlain && DT == kF32 && E >= 4 && R >= 1;
+  return (MODE == kPlain || MODE == kHadamard) && DT == kF32 && E >= 4 && R >= 1;
 }
 
 // Load E consecutive elements at element t0 + off (16-byte aligned for E >= 8

@@ -195,13 +195,16 @@ def unpack_dequant(codes: torch.Tensor, scales: torch.Tensor, n: int, bitwidth: 
 def hadamard_quantize_pack(x: torch.Tensor, bitwidth: int, block_size: int,
                            stochastic: bool = False, seed: int = 0, index_offset: int = 0,
                            codes: Optional[torch.Tensor] = None,
-                           scales: Optional[torch.Tensor] = None):
+                           scales: Optional[torch.Tensor] = None, input_reused: bool = False):
     """Blockwise Walsh-Hadamard transform of x, then compress; a partial last
-    block (x.numel() not a multiple of block_size) is compressed untransformed."""
+    block (x.numel() not a multiple of block_size) is compressed untransformed.
+
+    input_reused: as for quantize_pack (LOWBIT_HINT_INPUT_REUSED)."""
     n = x.numel()
     codes = _out_codes(n, bitwidth, x, codes)
     scales = _out_scales(n, block_size, x, scales)
-    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset)
+    qp = _qp(bitwidth, block_size, stochastic, seed, index_offset,
+             HINT_INPUT_REUSED if input_reused else 0)
     _check(lib().lowbit_hadamard_quantize_pack(_dev(x, "x"), _dtype_code(x), n, ctypes.byref(qp),
                                                _dev(codes, "codes"), _dev(scales, "scales"),
                                                _stream(x)), "lowbit_hadamard_quantize_pack")
