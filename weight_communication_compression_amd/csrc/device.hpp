@@ -310,6 +310,16 @@ __device__ __forceinline__ uint32_t fmix32_after_first_step(uint32_t h) {
 // in one bit b; flipping bit b of c ^ j changes the product by +-K1 * 2^b,
 // plus when the bit becomes set.  d[b] = (1 - 2 c_b) K1 2^b is the change
 // when bit b of j goes from 0 to 1.
+// All ones where bit b of x is set, else zero (v_bfe_i32).  Written as one
+// instruction the compiler cannot see through, so that a conditional negation
+// built on it stays two integer operations instead of a select between two
+// constants that it would reload into registers for every use.
+__device__ __forceinline__ uint32_t bit_mask(uint32_t x, int b) {
+  uint32_t m;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(x), "i"(b));
+  return m;
+}
+
 template <int N>
 struct GrayProducts {
   static constexpr int LOG2N = N <= 1 ? 0 : N <= 2 ? 1 : N <= 4 ? 2 : N <= 8 ? 3 : 4;
@@ -319,8 +329,11 @@ struct GrayProducts {
   __device__ __forceinline__ explicit GrayProducts(uint32_t c) {
     p = c * kFmixK1;                // j = 0
 #pragma unroll
-    for (int b = 0; b < LOG2N; ++b)
-      d[b] = ((c >> b) & 1u) ? 0u - (kFmixK1 << b) : (kFmixK1 << b);
+    for (int b = 0; b < LOG2N; ++b) {
+      // m: all ones when bit b of c is set; (K ^ m) - m = -K or K
+      const uint32_t m = bit_mask(c, b);
+      d[b] = ((kFmixK1 << b) ^ m) - m;
+    }
   }
   // the j of step k, and the product for it (step k >= 1 follows step k - 1)
   static constexpr int index(int k) { return k ^ (k >> 1); }
@@ -332,6 +345,34 @@ struct GrayProducts {
 };
 __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return fmix32_after_first_step(h ^ (h >> 16));
+}
+
+// The stochastic-rounding hash of global element index i starts from
+// lo ^ fmix32(hi ^ key), lo and hi the 32-bit halves of i.  For the indices
+// base + k (0 <= k < 2^32, base wave-uniform) hi is base's high half or one
+// more, so both high-half terms are computed once in scalar registers and
+// each lane picks one by the carry out of its low half.
+struct HiMix {
+  uint32_t lo0, m0, m1;
+  __device__ __forceinline__ HiMix(uint64_t base, uint32_t key)
+      : lo0((uint32_t)base),
+        m0(fmix32((uint32_t)(base >> 32) ^ key)),
+        m1(fmix32(((uint32_t)(base >> 32) + 1u) ^ key)) {}
+  // lo ^ fmix32(hi ^ key) of index base + k
+  __device__ __forceinline__ uint32_t x0(uint32_t k) const {
+    const uint32_t lo = lo0 + k;
+    return lo ^ (lo < lo0 ? m1 : m0);
+  }
+};
+
+// floor(y) as an int32 in one instruction (v_cvt_flr_i32_f32; the compiler
+// emits v_floor_f32 + v_cvt_i32_f32 for (int)floorf(y)).  Measured on gfx950
+// with binary32 denormals kept: negative subnormals give -1 and -0 gives 0,
+// as floorf; values beyond the int32 range saturate; NaN gives INT32_MAX.
+__device__ __forceinline__ int floor_to_int(float y) {
+  int q;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(y));
+  return q;
 }
 
 // ---------------------------------------------------------------- loads --

@@ -117,6 +117,7 @@ __device__ __forceinline__ void quantize_tile(
 
   // ---- codes and packing ---------------------------------------------------
   uint32_t* const cbase = o.codes + t0 / E;           // the tile's first word
+  const HiMix hm(o.index_offset + (uint64_t)t0, o.key);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t wl = (uint32_t)(r * kWave + lane);  // word within the tile
@@ -129,7 +130,10 @@ __device__ __forceinline__ void quantize_tile(
         for (int j = 0; j < E; ++j) deq[r][j] = signed_scale(word, j, sc.s);
       }
     } else {
-      word = G::PACK_BIAS;
+      // SR packs the codes' signed integer values onto the offset of every
+      // field (FLIP); nearest rounding packs bit patterns of q + kMagic onto
+      // PACK_BIAS.  Either way the fields never carry into one another.
+      word = SR ? G::FLIP : G::PACK_BIAS;
       // SR: h_j = fmix32((lo + j) ^ hk) for the word's elements j < E.  lo
       // (the low half of the first element's global index) is a multiple of
       // E, so lo + j = lo ^ j, and j < 2^16 leaves x >> 16 unchanged: the
@@ -139,8 +143,7 @@ __device__ __forceinline__ void quantize_tile(
       // packing adds are exact, so the order does not change the word.
       uint32_t c = 0;
       if constexpr (SR) {
-        const uint64_t gi = o.index_offset + (uint64_t)i0;
-        const uint32_t x0 = (uint32_t)gi ^ fmix32((uint32_t)(gi >> 32) ^ o.key);
+        const uint32_t x0 = hm.x0(wl * (uint32_t)E);
         c = x0 ^ (x0 >> 16);
       }
       GrayProducts<E> gp(c);
@@ -149,23 +152,24 @@ __device__ __forceinline__ void quantize_tile(
         const int j = GrayProducts<E>::index(k);
         if (k > 0) gp.step(k);
         const float x = v[r][j] * inv;
-        float q;
         if constexpr (SR) {
           const uint32_t h = GRAY ? fmix32_after_first_multiply(gp.p)
                                   : fmix32_after_first_step(c ^ (uint32_t)j);
           // the random offset (h >> 8) * 2^-24 is exact, so the fused form
           // rounds once, exactly like adding it in binary32.
           const float y = __builtin_fmaf((float)(h >> 8), 0x1p-24f, x);
-          q = __builtin_amdgcn_fmed3f(floorf(y), -QMAX, QMAX);
+          const int q = min(max(floor_to_int(y), -G::QMAX), G::QMAX);
+          word += (uint32_t)q << (j * BITS);
+          if constexpr (WANT_DEQ) deq[r][j] = (float)q * sc.s;
         } else {
           // clamp, then round: the same as rounding then clamping because the
           // bounds are integers; with |q| <= QMAX adding 1.5 * 2^23 rounds to
           // the nearest integer, ties to even.
-          q = __builtin_amdgcn_fmed3f(x, -QMAX, QMAX);
+          const float q = __builtin_amdgcn_fmed3f(x, -QMAX, QMAX);
+          const float t = q + kMagic;
+          word += __float_as_uint(t) << (j * BITS);
+          if constexpr (WANT_DEQ) deq[r][j] = (t - kMagic) * sc.s;
         }
-        const float t = q + kMagic;               // RTN: the rounding; SR: exact
-        word += __float_as_uint(t) << (j * BITS);
-        if constexpr (WANT_DEQ) deq[r][j] = (t - kMagic) * sc.s;
       }
     }
     if (full) {
