@@ -163,8 +163,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--next-rows", type=int, default=1,
-                    help="also time the extension kernels and the 4 MiB roundtrip alone "
-                         "(1) or not (0)")
+                    help="also time the extension kernels, the configurations, the 4 MiB "
+                         "roundtrip and the memory-system comparisons alone (1) or not (0)")
     ap.add_argument("--sweep", type=int, default=1,
                     help="with --next-rows 1, also time the 2^10..2^28 compress latency curve "
                          "(1) or not (0)")
@@ -175,7 +175,8 @@ def main() -> int:
                          "configuration, one thread and all threads (1) or not (0)")
     ap.add_argument("--only", default=None,
                     help="run only these measurements, '|'-separated: a group (next_rows, "
-                         "configs, compress_pattern) or one entry of next_rows or configs by its "
+                         "configs, compress_pattern, memory_patterns, block_sweep) or one entry of "
+                         "next_rows or configs by its "
                          "name; prints them as one JSON line instead of the step (for profiling "
                          "one workload at a time)")
     args = ap.parse_args()
@@ -458,6 +459,7 @@ def main() -> int:
     roundtrip = measure_roundtrip(L, dev) if args.next_rows else None
     configs = measure_configs(L, dev) if args.next_rows else None
     compress_pattern = measure_compress_pattern(L, dev, x) if args.next_rows else None
+    memory_patterns = measure_memory_patterns(L, dev) if args.next_rows else None
     sweep = measure_size_sweep(L, dev, args.cpu_sample > 0) if args.next_rows and args.sweep \
         else None
 
@@ -514,6 +516,8 @@ def main() -> int:
         out["configs"] = configs
     if compress_pattern is not None:
         out["compress_pattern"] = compress_pattern
+    if memory_patterns is not None:
+        out["memory_patterns"] = memory_patterns
     if sweep is not None:
         out["size_sweep"] = sweep
     print(json.dumps(out), flush=True)
@@ -544,6 +548,10 @@ def run_only(spec, L, lib, dev, stream, x, y):
     out["configs"] = measure_configs(L, dev, want=want("configs"))
     if "compress_pattern" in names:
         out["compress_pattern"] = measure_compress_pattern(L, dev, x)
+    if "memory_patterns" in names:
+        out["memory_patterns"] = measure_memory_patterns(L, dev)
+    if "block_sweep" in names:
+        out["block_sweep"] = measure_block_sweep(L, dev, x)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -704,6 +712,147 @@ def measure_compress_pattern(L, dev, x, reps=20):
                         "of_reference": round(cg / rg, 3)}
         del c, s
     del y
+    return out
+
+
+KNAME_PROBE = "void lowbit::stream_probe_kernel<{op}, {nt}>(lowbit::ProbeArgs, long)"
+
+
+def measure_block_sweep(L, dev, x, reps=7):
+    """Block sizes 32 .. 4096 at every bitwidth on the 64 Mi bucket (only with
+    --only block_sweep): compress (SR above 1 bit), decompress, EF compress,
+    Hadamard compress and decompress, and the
+    weight-difference compress of a 64 Mi bf16 shard, each alone after a
+    1 GiB read that leaves the Infinity Cache clean, median of `reps` (the
+    EF residual carries over from launch to launch); the fractions of
+    8 TB/s of each kernel's algorithmic bytes."""
+    import torch
+
+    N = x.numel()
+    gen = torch.Generator(device=dev).manual_seed(3)
+    w_old = (torch.randn(N, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    w_new = (w_old.float() + torch.randn(N, device=dev, generator=gen) * 1e-4).to(torch.bfloat16)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    e = torch.zeros(N, dtype=torch.float32, device=dev)   # the residual carries over
+
+    def median_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    def frac(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)
+
+    out = {}
+    for b in BITS:
+        for B in (32, 64, 128, 256, 512, 1024, 2048, 4096):
+            nw, nb = L.num_words(N, b), L.num_blocks(N, B)
+            c = torch.empty(nw, dtype=torch.int32, device=dev)
+            s = torch.empty(nb, dtype=torch.float16, device=dev)
+            alg = N * 4 + nw * 4 + nb * 2
+            sr = b > 1
+            row = {
+                "compress": frac(alg, median_ms(lambda: L.quantize_pack(x, b, B, sr, SEED, 0, c, s))),
+                "decompress": frac(alg, median_ms(lambda: L.unpack_dequant(c, s, N, b, B, out=y))),
+                "ef_compress": frac(alg + 8 * N, median_ms(
+                    lambda: L.ef_compress(x, e, b, B, sr, SEED, 0, c, s))),
+                "hadamard_compress": frac(alg, median_ms(
+                    lambda: L.hadamard_quantize_pack(x, b, B, sr, SEED, 0, codes=c, scales=s))),
+                "hadamard_decompress": frac(alg, median_ms(
+                    lambda: L.hadamard_unpack_dequant(c, s, N, b, B, out=y))),
+                "wdiff_compress": frac(4 * N + nw * 4 + nb * 2, median_ms(
+                    lambda: L.wdiff_compress(w_new, w_old, b, B, sr, SEED, 0, codes=c, scales=s))),
+            }
+            out[f"b{b} B{B}"] = row
+            del c, s
+    del w_old, w_new, flush, y, e
+    return out
+
+
+def measure_memory_patterns(L, dev, reps=7):
+    """The memory-system comparisons behind the codec kernels' launch shape
+    and store policy (lowbit_stream_probe_u32 and lowbit_fold_f32; not part of
+    `value`), each the median of `reps` launches timed alone, every launch
+    after a 1 GiB read that leaves the Infinity Cache clean:
+    * grid: 4 GiB read, write and copy of 32-bit words, one trip per wave
+      over the whole buffer against persistent grids of 2048 and 8192 waves
+      looping over it (streaming stores);
+    * drain: a 256 MiB read alone, right after a 256 MiB streaming write,
+      and right after a 256 MiB plain write (the write untimed, between the
+      flush and the read);
+    * write_stream: the same 256 MiB read alone against a pass that reads it
+      and writes 32 MiB (the 4-bit compress-volume fold of those bytes as
+      64 Mi binary32 values)."""
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def median_ms(fn, pre=None):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            if pre is not None:
+                pre()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    NW = 1 << 30                                   # 4 GiB of words
+    a = torch.empty(NW, dtype=torch.int32, device=dev)
+    b = torch.empty(NW, dtype=torch.int32, device=dev)
+    L.stream_probe(L.PROBE_WRITE, a, value=0x9E3779B9)
+    rd = torch.empty(NW // 1024, dtype=torch.int32, device=dev)
+    grid = {}
+    for waves in (0, 2048, 8192):
+        r = median_ms(lambda: L.stream_probe(L.PROBE_READ, rd, a, waves=waves))
+        w = median_ms(lambda: L.stream_probe(L.PROBE_WRITE, b, waves=waves))
+        c = median_ms(lambda: L.stream_probe(L.PROBE_COPY, b, a, waves=waves))
+        key = "one_trip_per_wave" if waves == 0 else f"persistent_{waves}_waves"
+        grid[key] = {"read_us": round(r * 1e3, 1), "read_GBps": gbps(4 * NW, r),
+                     "write_us": round(w * 1e3, 1), "write_GBps": gbps(4 * NW, w),
+                     "copy_us": round(c * 1e3, 1), "copy_GBps": gbps(8 * NW, c)}
+    S = 1 << 26                                    # 256 MiB of words
+    ra, wb = a[:S], b[:S]
+    rd2 = rd[:S // 1024]
+    read = lambda: L.stream_probe(L.PROBE_READ, rd2, ra)
+    alone = median_ms(read)
+    after_nt = median_ms(read, pre=lambda: L.stream_probe(L.PROBE_WRITE, wb, nontemporal=True))
+    after_plain = median_ms(read, pre=lambda: L.stream_probe(L.PROBE_WRITE, wb, nontemporal=False))
+    fold_out = torch.empty(L.num_words(S, 4), dtype=torch.int32, device=dev)
+    fold = median_ms(lambda: L.fold_f32(ra.view(torch.float32), 4, fold_out))
+    out = {
+        "grid": grid,
+        "drain": {"read_256MiB_alone_us": round(alone * 1e3, 1),
+                  "after_streaming_write_us": round(after_nt * 1e3, 1),
+                  "after_plain_write_us": round(after_plain * 1e3, 1)},
+        "write_stream": {"read_256MiB_us": round(alone * 1e3, 1),
+                         "read_256MiB_write_32MiB_us": round(fold * 1e3, 1)},
+        "kernels": {"read": KNAME_PROBE.format(op=0, nt="true"),
+                    "write_streaming": KNAME_PROBE.format(op=1, nt="true"),
+                    "write_plain": KNAME_PROBE.format(op=1, nt="false"),
+                    "copy": KNAME_PROBE.format(op=2, nt="true"),
+                    "fold": kname_fold(4)},
+    }
+    del a, b, rd, fold_out, flush
     return out
 
 

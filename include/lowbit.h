@@ -319,6 +319,33 @@ lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nst
 lowbit_status lowbit_fold_f32(const float* x, int64_t n, int32_t bitwidth, uint32_t* out,
                               hipStream_t stream);
 
+/*
+ * Measurement aid, not a step of the method: one pass over nwords 32-bit
+ * words with a chosen grid and store policy, the probe behind the codec
+ * kernels' launch shape (one trip per wave rather than a persistent grid) and
+ * their streaming stores.  A trip is 1024 consecutive words, four coalesced
+ * 16-byte pieces per lane.
+ *   op LOWBIT_PROBE_READ  : dst[t] = XOR of the words of trip t of src
+ *                           (nwords / 1024 words written);
+ *   op LOWBIT_PROBE_WRITE : dst[i] = (i mod 2^32) ^ value (src unused);
+ *   op LOWBIT_PROBE_COPY  : dst[i] = src[i].
+ *   waves       : 0 -- one trip per wave over the whole buffer (the codec
+ *                 kernels' shape); > 0 -- a persistent grid of that many waves
+ *                 (rounded up to whole workgroups of four) looping over the
+ *                 trips.
+ *   nontemporal : nonzero -- streaming (non-temporal) stores; 0 -- plain.
+ *   src, dst    : device, 16-byte aligned; must not overlap.
+ * Errors: EINVAL for an unknown op, nwords < 0 or not a multiple of 1024,
+ * waves < 0, or a null or misaligned pointer that the op uses when
+ * nwords > 0; nwords == 0 is a no-op.
+ */
+#define LOWBIT_PROBE_READ 0
+#define LOWBIT_PROBE_WRITE 1
+#define LOWBIT_PROBE_COPY 2
+lowbit_status lowbit_stream_probe_u32(int32_t op, const uint32_t* src, uint32_t* dst,
+                                      int64_t nwords, uint32_t value, int32_t waves,
+                                      int32_t nontemporal, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,6 +110,13 @@ def test_null_pointers_and_negative_sizes():
     assert L.lowbit_copy_f32(None, None, 10, None) == lb.EINVAL
     assert L.lowbit_copy_f32(None, None, -10, None) == lb.EINVAL
     assert L.lowbit_fold_f32(None, 10, 4, None, None) == lb.EINVAL
+    # memory-system probe: unknown op, a size that is not whole trips,
+    # negative waves, null pointers
+    assert L.lowbit_stream_probe_u32(3, None, None, 1024, 0, 0, 1, None) == lb.EINVAL
+    assert L.lowbit_stream_probe_u32(0, None, None, 1000, 0, 0, 1, None) == lb.EINVAL
+    assert L.lowbit_stream_probe_u32(1, None, None, 1024, 0, -1, 1, None) == lb.EINVAL
+    assert L.lowbit_stream_probe_u32(1, None, None, 1024, 0, 0, 1, None) == lb.EINVAL
+    assert L.lowbit_stream_probe_u32(2, None, None, 0, 0, 0, 1, None) == lb.OK
     assert L.lowbit_fold_f32(None, -1, 4, None, None) == lb.EINVAL
     assert L.lowbit_fold_f32(ctypes.c_void_p(0x1000), 10, 3, ctypes.c_void_p(0x2000), None) \
         == lb.EINVAL

@@ -48,6 +48,8 @@ def bench_kernel_names():
               bench.kname_reduce(4, 4, 7, False),           # 8 x 32 Mi reduce
               bench.kname_reduce(4, 4, 7, False, sum_out=True),
               bench.KNAME_XOR, bench.KNAME_COPY, bench.KNAME_ADD]
+    names += [bench.KNAME_PROBE.format(op=op, nt=nt)                 # memory_patterns
+              for op, nt in ((0, "true"), (1, "true"), (1, "false"), (2, "true"))]
     return names
 
 

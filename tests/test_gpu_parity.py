@@ -412,6 +412,29 @@ def test_add_inplace_reference_kernel():
         assert_same(f32_np(y), yh + xh, f"add n={n}")
 
 
+@pytest.mark.parametrize("nt", [True, False])
+@pytest.mark.parametrize("waves", [0, 8, 1000])
+def test_stream_probe_kernel(waves, nt):
+    """The memory-system probe: read (XOR of each 1024-word trip), write
+    (i ^ value) and copy, one trip per wave and persistent grids of fewer and
+    more waves than trips, streaming and plain stores."""
+    for ntrips in [1, 37, 1025]:
+        n = ntrips * 1024
+        h = np.random.default_rng(ntrips + waves).integers(0, 2 ** 32, n, dtype=np.uint32)
+        src = torch.from_numpy(h.view(np.int32)).cuda()
+        rd = torch.full((ntrips,), -1, dtype=torch.int32, device="cuda")
+        wr = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        cp = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        say(f"stream probe ntrips={ntrips} waves={waves} nt={nt}")
+        L.stream_probe(L.PROBE_READ, rd, src, waves=waves, nontemporal=nt)
+        L.stream_probe(L.PROBE_WRITE, wr, value=0x12345678, waves=waves, nontemporal=nt)
+        L.stream_probe(L.PROBE_COPY, cp, src, waves=waves, nontemporal=nt)
+        torch.cuda.synchronize()
+        assert_same(codes_np(rd), np.bitwise_xor.reduce(h.reshape(ntrips, 1024), axis=1), "read")
+        assert_same(codes_np(wr), np.arange(n, dtype=np.uint32) ^ np.uint32(0x12345678), "write")
+        assert_same(codes_np(cp), h, "copy")
+
+
 def _fold_reference(xh, bits):
     """The compress-volume reference's output, from its documented layout:
     groups of 2048 values as 8 rows x 64 lanes x 4, each lane's 32 values

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "liblowbit.so")
 
 SOURCES = ["api.cpp", "quantize_plain.hip", "quantize_ef.hip", "quantize_wdiff.hip",
            "quantize_ef21.hip", "quantize_hadamard.hip", "reduce.hip", "reduce_ef.hip", "reduce_mixed.hip",
-           "dequant.hip"]
+           "dequant.hip", "measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -319,6 +319,21 @@ lowbit_status lowbit_xor_streams_u32(const uint32_t* const* streams, int32_t nst
   return launch_xor_streams(a, stream);
 }
 
+lowbit_status lowbit_stream_probe_u32(int32_t op, const uint32_t* src, uint32_t* dst,
+                                     int64_t nwords, uint32_t value, int32_t waves,
+                                     int32_t nontemporal, hipStream_t stream) {
+  if (op < LOWBIT_PROBE_READ || op > LOWBIT_PROBE_COPY) return LOWBIT_EINVAL;
+  if (nwords < 0 || nwords > kMaxN || nwords % 1024 != 0 || waves < 0) return LOWBIT_EINVAL;
+  if (nwords == 0) return LOWBIT_OK;
+  if (!dst || !aligned(dst, 16)) return LOWBIT_EINVAL;
+  if (op != LOWBIT_PROBE_WRITE && (!src || !aligned(src, 16))) return LOWBIT_EINVAL;
+  ProbeArgs a{};
+  a.src = src;
+  a.dst = dst;
+  a.value = value;
+  return launch_stream_probe(op, a, nwords, waves, nontemporal != 0, stream);
+}
+
 lowbit_status lowbit_fold_f32(const float* x, int64_t n, int32_t bitwidth, uint32_t* out,
                               hipStream_t stream) {
   if (n < 0 || n > kMaxN) return LOWBIT_EINVAL;

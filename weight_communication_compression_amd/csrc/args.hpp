@@ -53,4 +53,12 @@ struct XorArgs {
   int32_t nstreams;
 };
 
+// Memory-system probe (measurement aid): operation codes and arguments.
+enum ProbeOp : int { kProbeRead = 0, kProbeWrite = 1, kProbeCopy = 2 };
+struct ProbeArgs {
+  const uint32_t* src;
+  uint32_t* dst;
+  uint32_t value;
+};
+
 }  // namespace lowbit

@@ -16,9 +16,10 @@ namespace lowbit {
 
 // Workgroups for a kernel in which each wave takes one trip of work (one wave
 // per trip); the kernels loop over whatever the cap of grid_blocks leaves.
-// (On MI355X a grid that walks memory once, in order, sustains far more HBM
-// bandwidth than a persistent grid-stride loop: measured 6.8 vs 5-6 TB/s
-// reads, 6.9 vs 4.3-5.1 TB/s writes.)
+// (On MI355X a grid that walks memory once, in order, sustains more HBM
+// bandwidth than a persistent grid-stride loop: with lowbit_stream_probe_u32
+// on 4 GiB, 6.2 vs 5.2-5.8 TB/s reads, 6.0 vs 5.0-5.1 TB/s writes, 5.7 vs
+// 4.9-5.4 TB/s copy for persistent grids of 2048 and 8192 waves.)
 template <int THREADS = kBlockThreads>
 inline int64_t grid_for_tiles(int64_t ntrips) {
   return grid_blocks(ntrips, THREADS);
@@ -65,6 +66,11 @@ lowbit_status launch_copy(const float* x, float* y, int64_t n, hipStream_t s);
 lowbit_status launch_add_inplace(const float* x, float* y, int64_t n, hipStream_t s);
 lowbit_status launch_xor_streams(const XorArgs& a, hipStream_t s);
 lowbit_status launch_fold(const float* x, int64_t n, int bits, uint32_t* out, hipStream_t s);
+// memory-system probe: op (ProbeOp) over nwords words (a multiple of 1024);
+// waves = 0: one trip per wave, else that many waves looping; nt: streaming
+// stores
+lowbit_status launch_stream_probe(int op, const ProbeArgs& a, int64_t nwords, int64_t waves,
+                                  bool nt, hipStream_t s);
 
 }  // namespace lowbit
 

@@ -21,10 +21,12 @@ __all__ = [
     "LowbitError", "lib", "library_path", "num_words", "num_blocks", "QParams",
     "quantize_pack", "unpack_dequant", "ef_compress", "reduce_requant",
     "wdiff_compress", "wdiff_apply", "copy_f32", "xor_streams", "add_inplace_f32", "fold_f32",
+    "stream_probe", "PROBE_READ", "PROBE_WRITE", "PROBE_COPY",
     "OK", "EINVAL", "EUNSUPPORTED", "EDEVICE", "F32", "BF16", "HINT_INPUT_REUSED",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, 1, 2, 3
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
 F32, BF16 = 0, 1
 HINT_INPUT_REUSED = 1        # lowbit_qparams.hints: the input is read again soon
 
@@ -78,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "lowbit_xor_streams_u32": (ctypes.c_int, [P, i32, i64, P, P]),
             "lowbit_add_inplace_f32": (ctypes.c_int, [P, P, i64, P]),
             "lowbit_fold_f32": (ctypes.c_int, [P, i64, i32, P, P]),
+            "lowbit_stream_probe_u32": (ctypes.c_int, [i32, P, P, i64, ctypes.c_uint32, i32, i32, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -418,3 +421,24 @@ def fold_f32(x: torch.Tensor, bitwidth: int, out: Optional[torch.Tensor] = None)
     _check(lib().lowbit_fold_f32(_dev(x, "x"), n, int(bitwidth), _dev(out, "out"), _stream(x)),
            "lowbit_fold_f32")
     return out
+
+
+def stream_probe(op: int, dst: torch.Tensor, src: Optional[torch.Tensor] = None, value: int = 0,
+                 waves: int = 0, nontemporal: bool = True) -> torch.Tensor:
+    """Memory-system probe (not a codec step), on int32 tensors viewed as
+    32-bit words: PROBE_READ writes dst[t] = XOR of trip t (1024 words) of
+    src, PROBE_WRITE dst[i] = i ^ value, PROBE_COPY dst = src.  waves = 0:
+    one trip per wave; > 0: a persistent grid of that many waves."""
+    nwords = src.numel() if op != PROBE_WRITE else dst.numel()
+    for t, name in ((dst, "dst"), (src, "src")):
+        if t is not None and t.dtype != torch.int32:
+            raise LowbitError(EINVAL, f"{name} must be int32")
+    if op == PROBE_READ and dst.numel() < nwords // 1024:
+        raise LowbitError(EINVAL, "dst too small")
+    if op == PROBE_COPY and dst.numel() < nwords:
+        raise LowbitError(EINVAL, "dst too small")
+    sp = _dev(src, "src") if src is not None else None
+    _check(lib().lowbit_stream_probe_u32(int(op), sp, _dev(dst, "dst"), nwords,
+                                         int(value) & 0xFFFFFFFF, int(waves), int(bool(nontemporal)),
+                                         _stream(dst)), "lowbit_stream_probe_u32")
+    return dst
